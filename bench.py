@@ -1,0 +1,304 @@
+"""Benchmark: paged-attention decode step on one MI355X.
+
+Default workload (the configuration the headline metric is quoted on): 256
+sequences with log-normal lengths (median 200, sigma 1, clipped to [16, 2048]),
+32 query / 8 key-value heads, head_dim 128, bf16.  One step = append one K/V
+row per sequence (kv_append), then decode one query per sequence over the grown
+cache, then roll the lengths back on the host so every step sees the same
+workload.  Steps rotate over several pool replicas so that the working set
+(~0.4 GB per replica) streams from HBM rather than the 256 MB Infinity Cache.
+
+Prints one JSON line.  `value` is effective GB/s of the whole step (algorithmic
+bytes of append + decode / step time); `roofline` reports the attention kernel
+alone, timed with HIP events recorded on the launch stream; `cpu_baseline` times
+the float64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn decode effective HBM GB/s (% of MI355X peak); µs/step at batch 256"
+PEAK_GBS = 8000.0  # MI355X HBM3E, AMD public specification
+FILL = {"f32": 0x7FBADBAD, "f16": 0x7E5A, "bf16": 0x7FDA}
+EB = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="highbatch", choices=["highbatch", "gqa70b", "long", "verify", "tiny"])
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile-events", action="store_true",
+                    help="do not record HIP events around the attention kernel")
+    return ap.parse_args()
+
+
+def to_torch(arr, dtype, device="cuda"):
+    import torch
+    arr = np.ascontiguousarray(arr)
+    if dtype == "bf16":
+        t = torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16)
+    elif dtype == "f16":
+        t = torch.from_numpy(arr.view(np.float16))
+    else:
+        t = torch.from_numpy(arr.view(np.float32))
+    return t.to(device)
+
+
+def step_lengths(w):
+    """Cached tokens per sequence when the attention runs."""
+    return [int(n) for n in w.final_lengths()]
+
+
+def decode_bytes(w) -> int:
+    """Algorithmic bytes of one attention launch: every K and V row of every KV
+    head once (a shared prefix once), Q read, O written, block-table entries used
+    and one length per sequence."""
+    lens = step_lengths(w)
+    e = EB[w.dtype]
+    rows = sum(n - w.prefix_len for n in lens) + (w.prefix_len if lens else 0)
+    kv = rows * w.num_kv_heads * w.head_dim * e * 2
+    qo = 2 * len(lens) * w.k_draft * w.num_q_heads * w.head_dim * e
+    tab = sum(math.ceil(n / 16) for n in lens) * 4 + 4 * len(lens)
+    return kv + qo + tab
+
+
+def append_bytes(w) -> int:
+    if w.new_k is None or w.mode not in ("append_decode", "verify"):
+        return 0
+    rows = w.new_k.shape[0] * w.new_k.shape[1]
+    return 4 * rows * w.num_kv_heads * w.head_dim * EB[w.dtype] + 4 * rows
+
+
+class Replica:
+    """One filled pool plus the pre-marshalled arguments of a step."""
+
+    def __init__(self, w, pt):
+        import torch
+        from paged_kv_cache_216_amd.cache import PagedKVCache
+
+        self.w = w
+        b = w.batch
+        self.cache = PagedKVCache(w.num_blocks, w.num_kv_heads, w.head_dim, w.dtype, b, w.max_blocks_per_seq,
+                                  free_order=w.free_order, fill_bits=FILL[w.dtype])
+        c = self.cache
+        if w.prefix_len:
+            c.alloc(0)
+            c.append([0], [w.prefix_len], to_torch(w.prefix_k, w.dtype), to_torch(w.prefix_v, w.dtype))
+            for s in range(1, b):
+                c.alloc(s, 0, w.prefix_len)
+        else:
+            for s in range(b):
+                c.alloc(s)
+        for lo in range(0, b, 32):
+            grp = list(range(lo, min(b, lo + 32)))
+            ns = [int(w.lengths[i]) for i in grp]
+            c.append(grp, ns, to_torch(np.concatenate([w.k_rows[i] for i in grp]), w.dtype),
+                     to_torch(np.concatenate([w.v_rows[i] for i in grp]), w.dtype))
+        torch.cuda.synchronize()
+        self.base_lens = [int(w.lengths[i]) + w.prefix_len for i in range(b)]
+        self.ids = (ctypes.c_int32 * b)(*range(b))
+        self.t_new = 0
+        if w.new_k is not None and w.mode in ("append_decode", "verify"):
+            self.t_new = w.new_k.shape[1]
+            self.ntok = (ctypes.c_int32 * b)(*([self.t_new] * b))
+            hk = w.new_k.reshape(-1, w.num_kv_heads, w.head_dim)
+            hv = w.new_v.reshape(-1, w.num_kv_heads, w.head_dim)
+            self.k_new = to_torch(hk, w.dtype)
+            self.v_new = to_torch(hv, w.dtype)
+            self.rollback = (ctypes.c_int32 * b)(*self.base_lens)
+        q = to_torch(w.q, w.dtype)
+        self.q = q if w.k_draft > 1 else q[:, 0].contiguous()
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[:-1], dtype=torch.float32, device="cuda")
+        max_len = max(step_lengths(w))
+        self.ws = c.make_workspace(b, w.num_q_heads, max_len, k_draft=w.k_draft, partition_tokens=pt)
+        self.ws_bytes = 0 if self.ws is None else self.ws.numel() * 4
+        self.pt = pt
+
+    def step(self, stream_handle):
+        from paged_kv_cache_216_amd import abi
+        c, w, lib = self.cache, self.w, self.cache.lib
+        h = c.handle
+        vp = ctypes.c_void_p
+        if self.t_new:
+            abi.check(lib.pa_append_kv(h, self.ids, w.batch, self.ntok, vp(self.k_new.data_ptr()),
+                                       vp(self.v_new.data_ptr()), stream_handle))
+        ws = None if self.ws is None else vp(self.ws.data_ptr())
+        if w.k_draft == 1:
+            rc = lib.pa_decode(h, self.ids, w.batch, w.num_q_heads, w.scale, vp(self.q.data_ptr()),
+                               vp(self.out.data_ptr()), vp(self.lse.data_ptr()), self.pt, ws, self.ws_bytes,
+                               stream_handle)
+        else:
+            rc = lib.pa_verify(h, self.ids, w.batch, w.k_draft, w.num_q_heads, w.scale, vp(self.q.data_ptr()),
+                               vp(self.out.data_ptr()), vp(self.lse.data_ptr()), self.pt, ws, self.ws_bytes,
+                               stream_handle)
+        abi.check(rc)
+        if self.t_new:
+            abi.check(lib.pa_truncate_batch(h, self.ids, w.batch, self.rollback))
+
+
+def make_workload(name):
+    from workloads import by_name
+    return by_name(name)
+
+
+def describe(w) -> str:
+    d = {"highbatch": "256 seqs, lengths lognormal(median 200, sigma 1) clipped to [16, 2048], 32 q / 8 kv heads, "
+                      "head_dim 128, bf16; step = append 1 row/seq + decode",
+         "gqa70b": "32 seqs, lengths U[512, 4096], 64 q / 8 kv heads, head_dim 128, fp16; step = decode",
+         "long": "8 seqs x 32768 tokens, 32 q / 8 kv heads, head_dim 128, fp16, 512-token split-KV; step = decode",
+         "verify": "64 seqs sharing a 4096-token copy-on-write prefix + suffix U[16, 512], 32 q / 8 kv heads, "
+                   "head_dim 128, bf16; step = append 5 drafts/seq + causal verify",
+         "tiny": "4 seqs {17, 33, 64, 100}, 4 heads, head_dim 64, fp32; step = append + decode"}
+    return d[w.name]
+
+
+def cpu_baseline(w, budget_s):
+    """The float64 oracle, single-threaded, on the first sequences of the same
+    workload until `budget_s` seconds of work; reported in the metric's unit."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as A
+    from oracle.allocator import PoolModel
+
+    lens = step_lengths(w)
+    done_bytes, elapsed, nseq, ntok = 0, 0.0, 0, 0
+    with threadpool_limits(limits=1):
+        for s in range(w.batch):
+            m = PoolModel(w.num_blocks, w.num_kv_heads, w.head_dim, w.dtype, 1, w.max_blocks_per_seq,
+                          free_order=w.free_order)
+            m.alloc(0)
+            parts_k, parts_v = [], []
+            if w.prefix_len:
+                parts_k.append(w.prefix_k)
+                parts_v.append(w.prefix_v)
+            parts_k.append(w.k_rows[s])
+            parts_v.append(w.v_rows[s])
+            if w.new_k is not None and w.mode in ("append_decode", "verify"):
+                parts_k.append(w.new_k[s])
+                parts_v.append(w.new_v[s])
+            k, v = np.concatenate(parts_k), np.concatenate(parts_v)
+            t0 = time.perf_counter()
+            m.append([0], [k.shape[0]], k, v)
+            if w.k_draft == 1:
+                A.decode_from_pool(m.kpool, m.vpool, m.table(0), m.length(0), w.q[s, 0], w.scale, w.dtype)
+            else:
+                A.verify_from_pool(m.kpool, m.vpool, m.table(0), m.length(0), w.q[s], w.scale, w.dtype)
+            elapsed += time.perf_counter() - t0
+            n = lens[s]
+            done_bytes += (n * w.num_kv_heads * w.head_dim * EB[w.dtype] * 2
+                           + 2 * w.k_draft * w.num_q_heads * w.head_dim * EB[w.dtype] + math.ceil(n / 16) * 4 + 4)
+            nseq += 1
+            ntok += n
+            if elapsed >= budget_s:
+                break
+    return {
+        "value": round(done_bytes / elapsed / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"first {nseq} of {w.batch} sequences ({ntok} cached tokens): append into the float64 "
+                  f"oracle's pool model, then gather + softmax attention; one thread; {elapsed:.1f} s",
+        "cpu": platform.processor() or platform.machine(), "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(sharding by sequence or by key/value head is not implemented)", flush=True)
+        sys.exit(2)
+    import torch
+
+    from paged_kv_cache_216_amd import abi
+    abi.load()
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    torch.cuda.set_device(0)
+    w = make_workload(args.workload)
+    pt = args.partition_tokens if args.partition_tokens else (w.partition_tokens or 0)
+    print(f"bench: building {args.replicas} replica pools for '{w.name}'", file=sys.stderr, flush=True)
+    reps = [Replica(w, pt) for _ in range(args.replicas)]
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    for i in range(args.warmup):
+        reps[i % len(reps)].step(sh)
+    torch.cuda.synchronize()
+    prof = not args.no_profile_events
+    for r in reps:
+        r.cache.profile_read(0)
+        r.cache.profile_read(1)
+        r.cache.profile_read(2)
+        r.cache.profile_enable(prof)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        reps[i % len(reps)].step(sh)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    kern = {0: [0.0, 0], 1: [0.0, 0], 2: [0.0, 0]}
+    for r in reps:
+        r.cache.profile_enable(False)
+        for k in kern:
+            ms, n = r.cache.profile_read(k)
+            kern[k][0] += ms
+            kern[k][1] += n
+    dec_b = decode_bytes(w)
+    app_b = append_bytes(w)
+    step_b = dec_b + app_b
+    value = step_b / (ms_step * 1e-3) / 1e9
+    roof = None
+    if kern[0][1]:
+        attn_ms = kern[0][0] / kern[0][1]
+        achieved = dec_b / (attn_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                "kernel": "attn_kernel (paged decode/verify)", "avg_us": round(attn_ms * 1e3, 2),
+                "bytes_per_launch": dec_b}
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "us_per_step": round(ms_step * 1e3, 2),
+        "pct_of_peak": round(100 * value / PEAK_GBS, 2), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: {describe(w)}", "batch": w.batch, "seed": w.seed,
+                   "replicas": args.replicas, "partition_tokens": pt or "library choice (512 when split)",
+                   "bytes_per_step": step_b, "decode_bytes": dec_b, "append_bytes": app_b,
+                   "cached_tokens": int(sum(step_lengths(w)))},
+        "kernel_us": {"attention": round(1e3 * kern[0][0] / max(1, kern[0][1]), 2),
+                      "merge": round(1e3 * kern[1][0] / max(1, kern[1][1]), 2) if kern[1][1] else None,
+                      "append": round(1e3 * kern[2][0] / max(1, kern[2][1]), 2) if kern[2][1] else None},
+        "host_wall_ms_per_step": round(1e3 * wall / args.steps, 4),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

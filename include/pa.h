@@ -1,0 +1,194 @@
+/*
+ * pa.h — paged KV-cache attention for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * What the library does, and where the pages define it:
+ *   - Each sequence's key/value cache is cut into fixed blocks of 16 tokens that
+ *     may sit anywhere in one physical pool; a per-sequence block table maps
+ *     logical blocks to physical ones and is resolved inside the attention
+ *     kernel ("PagedAttention, décodage spéculatif, MoE et Blackwell", section 1;
+ *     kenji.blog "llm-inference-optimization-kv-cache", section 4.1).
+ *   - Sequences that derive from the same prompt share physical blocks, copied
+ *     only when written (same page, section 1; kenji.blog page, section 4.2).
+ *   - A decode step stores the new token's K and V rows in the cache, then the
+ *     token's query attends over the whole cache (kenji.blog page, section 3.1
+ *     and its data-flow graph), a step bound by memory bandwidth because it
+ *     reads the entire cache ("CUDA Graphs, modèles de raisonnement et service
+ *     désagrégé", section 3 table).
+ *   - Speculative verify: K draft tokens are checked in one pass; after a
+ *     rejection the cache is cut back to the accepted prefix (kenji.blog page,
+ *     section 5.2; ranksignal.fr post 218, "Spéculer").
+ *
+ * Conventions for every function:
+ *   - Return PA_OK (0) or a negative pa_status.  No C++ exception crosses the ABI.
+ *     On any error the pool is left unchanged.  pa_last_error() gives a message
+ *     for the calling thread's most recent failure.
+ *   - "host" pointers are CPU memory read during the call only; "device"
+ *     pointers are GPU memory owned by the caller, which must stay valid until
+ *     the work enqueued on `stream` has finished.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     device work is asynchronous on that stream.  Calls on one pool must be
+ *     ordered: issue them from one thread, on one stream (or synchronise).
+ *   - A pool is not thread-safe.
+ *
+ * Physical layout (caller allocates; bit patterns are the contract):
+ *   element size e = 4 (PA_F32) or 2 (PA_F16, PA_BF16); X = 16 / e
+ *   K pool: [num_blocks][num_kv_heads][head_dim / X][16][X]
+ *   V pool: [num_blocks][num_kv_heads][head_dim][16]
+ *   so one (block, head) K or V page is 16 * head_dim * e contiguous bytes,
+ *   K stored in 16-byte chunks of X consecutive dims, slot-minor; V stored
+ *   dim-major with the 16 slots of one dim contiguous.
+ *   block_table_dev: int32 [max_seqs][max_blocks_per_seq]; entries
+ *   [0, ceil(len/16)) of a live sequence hold its physical blocks, others are
+ *   unspecified.  seq_len_dev: int32 [max_seqs], the length of each live
+ *   sequence, 0 for others.  Both mirrors are brought up to date by every
+ *   device call (pa_append_kv, pa_decode, pa_verify, pa_sync_tables).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct pa_pool pa_pool;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = -1, /* bad argument or unknown / duplicate sequence            */
+  PA_ERR_NOMEM = -2,   /* not enough free blocks (nothing was changed)            */
+  PA_ERR_HIP = -3,     /* a HIP runtime call or kernel launch failed              */
+  PA_ERR_STATE = -4    /* call not possible in this pool's state (e.g. host-only) */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Create a pool over caller-owned device memory.
+ *   num_blocks      physical blocks in k_pool / v_pool (> 0)
+ *   block_size      tokens per block; must be 16
+ *   num_kv_heads    key/value heads per block (> 0)
+ *   head_dim        64, 128 or 256
+ *   dtype           pa_dtype of K, V, Q and outputs
+ *   k_pool, v_pool  device, sized as in the layout above
+ *   block_table_dev device int32 [max_seqs * max_blocks_per_seq]
+ *   seq_len_dev     device int32 [max_seqs]
+ *   free_order      host int32 [num_blocks], a permutation of 0..num_blocks-1
+ *                   giving the order in which blocks are handed out; NULL
+ *                   means 0, 1, 2, ...
+ * If all four device pointers are NULL the pool is host-only: it keeps the
+ * block tables but enqueues no device work (pa_append_kv then takes NULL rows;
+ * pa_decode / pa_verify return PA_ERR_STATE).
+ * The library allocates, for the pool's lifetime, a small device buffer and a
+ * pinned host buffer for per-call metadata; it never allocates pool memory. */
+int pa_create_pool(pa_pool** out, int num_blocks, int block_size, int num_kv_heads,
+                   int head_dim, int dtype, void* k_pool, void* v_pool,
+                   int32_t* block_table_dev, int32_t* seq_len_dev, int max_seqs,
+                   int max_blocks_per_seq, const int32_t* free_order);
+
+/* Waits for the pool's outstanding metadata copies, then frees the library's
+ * own buffers.  Caller memory is not touched.  NULL is accepted. */
+int pa_destroy_pool(pa_pool* pool);
+
+/* Start sequence seq_id (0 <= seq_id < max_seqs, not live).  With
+ * parent_seq >= 0 (live, != seq_id) the new sequence shares the parent's first
+ * ceil(shared_tokens / 16) blocks (reference counts + 1) and starts with
+ * length shared_tokens (0 <= shared_tokens <= parent length): copy-on-write
+ * fork.  With parent_seq < 0, shared_tokens must be 0.  Host-side only; the
+ * device table rows are written by the next device call. */
+int pa_alloc_blocks(pa_pool* pool, int seq_id, int parent_seq, int shared_tokens);
+
+/* Append n_tok[i] new K/V rows to sequence seq_ids[i], i = 0..n_seq-1.
+ *   seq_ids, n_tok  host int32 [n_seq]; sequences live and distinct;
+ *                   n_tok[i] >= 0; length + n_tok[i] <= 16 * max_blocks_per_seq
+ *   k_new, v_new    device [sum(n_tok)][num_kv_heads][head_dim] in dtype, rows
+ *                   packed in call order
+ * Blocks are taken from the front of the free list, sequence by sequence,
+ * token by token.  Writing into a block that other sequences still reference
+ * first copies its filled slots into a fresh block (copy-on-write).  Fails
+ * with PA_ERR_NOMEM, changing nothing, if the free list cannot cover the
+ * call.  Stored bytes are bit-exact copies of the input rows. */
+int pa_append_kv(pa_pool* pool, const int32_t* seq_ids, int n_seq, const int32_t* n_tok,
+                 const void* k_new, const void* v_new, void* stream);
+
+/* One query token per sequence attends over all of its cached tokens.
+ *   seq_ids      host int32 [n_seq]; live, length >= 1 (repeats allowed)
+ *   num_q_heads  multiple of num_kv_heads; query head h reads key/value head
+ *                h / (num_q_heads / num_kv_heads); (num_q_heads/num_kv_heads)
+ *                at most 64 (32 when head_dim is 256)
+ *   scale        multiplies q.k before the softmax (typically 1/sqrt(head_dim))
+ *   q, out       device [n_seq][num_q_heads][head_dim] in dtype
+ *   lse          device float [n_seq][num_q_heads] (natural-log log-sum-exp of
+ *                the scaled scores) or NULL
+ *   partition_tokens  0 = library choice; otherwise a positive multiple of 32:
+ *                contexts longer than this are cut into partitions processed
+ *                in parallel and merged exactly by their log-sum-exp; a value
+ *                >= the longest context disables the split
+ *   workspace    device scratch for split partials, ws_bytes long (see
+ *                pa_workspace_size); may be NULL when no sequence is split.
+ *                With partition_tokens = 0 the library only splits when the
+ *                workspace is large enough.
+ * Softmax and accumulation are fp32; out is rounded to dtype (nearest even). */
+int pa_decode(pa_pool* pool, const int32_t* seq_ids, int n_seq, int num_q_heads, float scale,
+              const void* q, void* out, float* lse, int partition_tokens, void* workspace,
+              size_t ws_bytes, void* stream);
+
+/* Speculative verify: the last k_draft rows of each sequence are draft tokens
+ * (already appended) and draft i (0-based) attends to positions
+ * [0, length - k_draft + i], its own row included.
+ *   q, out  device [n_seq][k_draft][num_q_heads][head_dim]
+ *   lse     device float [n_seq][k_draft][num_q_heads] or NULL
+ * (num_q_heads / num_kv_heads) * k_draft is at most 64 (32 when head_dim is
+ * 256); lengths must be >= k_draft.  Other arguments as pa_decode.
+ * k_draft = 1 is exactly pa_decode. */
+int pa_verify(pa_pool* pool, const int32_t* seq_ids, int n_seq, int k_draft, int num_q_heads,
+              float scale, const void* q, void* out, float* lse, int partition_tokens,
+              void* workspace, size_t ws_bytes, void* stream);
+
+/* Cut sequence seq_id back to new_len tokens (0 <= new_len <= length), e.g. to
+ * drop rejected drafts.  Blocks past ceil(new_len / 16) lose one reference and
+ * go to the back of the free list, in logical order, when unreferenced. */
+int pa_truncate(pa_pool* pool, int seq_id, int new_len);
+
+/* pa_truncate for n_seq sequences in one call (host int32 arrays
+ * seq_ids[n_seq], new_lens[n_seq]), e.g. rolling a whole batch back to its
+ * accepted drafts.  All arguments are checked first; on error nothing changes. */
+int pa_truncate_batch(pa_pool* pool, const int32_t* seq_ids, int n_seq, const int32_t* new_lens);
+
+/* End sequence seq_id: pa_truncate to 0, then the id becomes free. */
+int pa_free_seq(pa_pool* pool, int seq_id);
+
+/* Enqueue the pending block-table / length updates on `stream` now. */
+int pa_sync_tables(pa_pool* pool, void* stream);
+
+/* Bytes of workspace that pa_decode / pa_verify need for n_seq sequences of
+ * at most max_tokens tokens each with this partition_tokens (0 = the library's
+ * choice) and k_draft queries per sequence (1 for decode).  0 if nothing splits. */
+int pa_workspace_size(const pa_pool* pool, int n_seq, int num_q_heads, int k_draft,
+                      int max_tokens, int partition_tokens, size_t* bytes);
+
+/* Host copies of the allocator state (for tests and schedulers). */
+int pa_get_block_table(const pa_pool* pool, int seq_id, int32_t* out, int cap, int* n_blocks,
+                       int* len);
+int pa_get_refcount(const pa_pool* pool, int block_id, int* rc);
+int pa_num_free_blocks(const pa_pool* pool, int* n);
+/* The free list, front first (out may be NULL to query the count). */
+int pa_get_free_list(const pa_pool* pool, int32_t* out, int cap, int* n);
+
+const char* pa_strerror(int status);
+const char* pa_last_error(void);
+
+/* Timing of the attention kernels: when enabled, HIP events are recorded on the
+ * call's stream around each attention-kernel launch.  pa_profile_read
+ * synchronises those events and returns the summed elapsed milliseconds and
+ * the number of launches since the last read (then resets).
+ * which: 0 = attention kernel (decode / verify), 1 = split merge kernel,
+ *        2 = append kernel. */
+int pa_profile_enable(pa_pool* pool, int on);
+int pa_profile_read(pa_pool* pool, int which, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H_ */

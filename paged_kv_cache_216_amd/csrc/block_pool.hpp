@@ -1,0 +1,87 @@
+// Host-side block allocator for the paged KV cache: free deque, per-block
+// reference counts, per-sequence block tables and lengths, copy-on-write
+// decisions, and the list of device-table entries that changed.
+//
+// Rules (the pages fix the first three; the rest is this library's reading):
+//  - fixed 16-token blocks placed anywhere, reached through a per-sequence table
+//    ("PagedAttention, décodage spéculatif, MoE et Blackwell", section 1);
+//  - only the blocks a sequence needs are taken (kenji.blog
+//    "llm-inference-optimization-kv-cache", section 4.2);
+//  - sequences from one prompt share blocks, copied on write (same sections);
+//  - free list = deque in a caller-given order, pop front, push back on release
+//    in increasing logical order; copy is lazy, on the first write into a block
+//    referenced more than once, and takes the slots already filled; sequences of
+//    one append are served in call order, token by token; an append that cannot
+//    get all the blocks it needs changes nothing.
+#pragma once
+
+#include <cstdint>
+#include <deque>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+namespace pa {
+
+constexpr int kBlock = 16;
+
+enum Status : int { kOk = 0, kInvalid = -1, kNoMem = -2, kHip = -3, kState = -4 };
+
+struct CowCopy {
+  int32_t src;
+  int32_t dst;
+  int32_t rows;  // slots [0, rows) are copied
+};
+
+class BlockPool {
+ public:
+  int init(int num_blocks, int max_seqs, int max_blocks_per_seq, const int32_t* free_order,
+           std::string* err);
+
+  int alloc(int seq, int parent, int shared_tokens, std::string* err);
+  // On success appends one slot (phys * 16 + offset) per row, in call order, to
+  // *slots, and the copies to perform before the rows are written to *cows.
+  int append(const int32_t* seqs, int n_seq, const int32_t* n_tok, std::vector<int32_t>* slots,
+             std::vector<CowCopy>* cows, std::string* err);
+  int truncate(int seq, int new_len, std::string* err);
+  int free_seq(int seq, std::string* err);
+
+  bool live(int seq) const { return seq >= 0 && seq < max_seqs_ && len_[seq] >= 0; }
+  int length(int seq) const { return len_[seq]; }
+  const std::vector<int32_t>& table(int seq) const { return tables_[seq]; }
+  int refcount(int block) const { return rc_[block]; }
+  int num_free() const { return static_cast<int>(free_.size()); }
+  const std::deque<int32_t>& free_list() const { return free_; }
+  int num_blocks() const { return num_blocks_; }
+  int max_seqs() const { return max_seqs_; }
+  int max_blocks_per_seq() const { return max_blocks_; }
+
+  // Device-mirror bookkeeping: entries (seq * max_blocks + j) and sequences
+  // whose device copy is stale.  take_dirty() returns them and clears the sets.
+  struct Dirty {
+    std::vector<int32_t> table_idx;    // flat indices into the device table
+    std::vector<int32_t> table_val;    // their current values
+    std::vector<int32_t> len_seq;      // sequences whose length changed
+    std::vector<int32_t> len_val;      // current length (0 if not live)
+  };
+  bool has_dirty() const { return !dirty_entries_.empty() || !dirty_lens_.empty(); }
+  void take_dirty(Dirty* out);
+
+ private:
+  int32_t pop();
+  void release(int32_t b);
+  void mark_entry(int seq, int j) { dirty_entries_.insert(seq * max_blocks_ + j); }
+  void mark_len(int seq) { dirty_lens_.insert(seq); }
+
+  int num_blocks_ = 0;
+  int max_seqs_ = 0;
+  int max_blocks_ = 0;
+  std::deque<int32_t> free_;
+  std::vector<int32_t> rc_;
+  std::vector<std::vector<int32_t>> tables_;
+  std::vector<int32_t> len_;  // -1 = not live
+  std::unordered_set<int32_t> dirty_entries_;
+  std::unordered_set<int32_t> dirty_lens_;
+};
+
+}  // namespace pa

@@ -1,0 +1,81 @@
+// Launch interface between the C-ABI layer (pa_api.cpp) and the gfx950 kernels
+// (kernels.hip).  Plain structs of device pointers and sizes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pa {
+
+enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+// One launch applies pending device-table updates, copy-on-write block copies
+// and the scatter of new rows.  Metadata (int32) lives in one device buffer:
+//   tab  [n_tab][2]  (flat table index, physical block)
+//   lens [n_len][2]  (sequence, length)
+//   cows [n_cow][3]  (src block, dst block, rows to copy)
+//   slots[n_rows]    (physical block * 16 + slot) for row r of k_new / v_new
+struct AppendParams {
+  void* k_pool;
+  void* v_pool;
+  int32_t* block_table;
+  int32_t* seq_len;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* tab;
+  const int32_t* lens;
+  const int32_t* cows;
+  const int32_t* slots;
+  int n_tab, n_len, n_cow, n_rows;
+  int hkv, head_dim, elem_bytes;
+};
+
+// Work unit of the attention kernel, one per (sequence, partition); the
+// key/value head comes from the grid.
+struct WorkUnit {
+  int32_t q_row;      // index of the sequence in q / out (0..n_seq-1)
+  int32_t seq;        // row of the block table
+  int32_t n;          // tokens in the sequence
+  int32_t tok_begin;  // first token of this partition (multiple of 32)
+  int32_t tok_end;    // one past the last token of this partition
+  int32_t slot_base;  // -1: write out/lse directly; else partial slot of kv head 0, part 0
+  int32_t nparts;     // partitions of this sequence
+  int32_t part;       // this unit's partition index
+};
+
+struct MergeUnit {
+  int32_t q_row;
+  int32_t slot_base;
+  int32_t nparts;
+  int32_t pad;
+};
+
+struct AttnParams {
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  int max_blocks;
+  int num_blocks;     // physical blocks; table entries are clamped into range
+  const void* q;
+  void* out;
+  float* lse;
+  float* ws_acc;      // [slot][R][D] unnormalised partial outputs
+  float* ws_ml;       // [slot][R][2] running max (log2 domain) and sum
+  const WorkUnit* units;
+  const MergeUnit* merges;
+  int n_units;
+  int n_merges;
+  int hkv, hq, group, k_draft, rows;  // rows = group * k_draft
+  int head_dim;
+  float scale_log2;   // scale * log2(e)
+};
+
+hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+// kernel_ms_event_*: optional events recorded around the attention launch
+hipError_t launch_attention(DType dt, const AttnParams& p, hipStream_t stream);
+hipError_t launch_merge(DType dt, const AttnParams& p, hipStream_t stream);
+// Largest supported rows (group * k_draft) for a head dim.
+int max_rows_for_head_dim(int head_dim);
+
+}  // namespace pa
