@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB before the timed region, so that "
+                         "memory counters can be scaled against a copy of known size")
     ap.add_argument("--no-profile-events", action="store_true",
                     help="do not record HIP events around the attention kernel")
     return ap.parse_args()
@@ -237,6 +240,14 @@ def main():
     reps = [Replica(w, pt) for _ in range(args.replicas)]
     stream = torch.cuda.current_stream()
     sh = ctypes.c_void_p(stream.cuda_stream)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         reps[i % len(reps)].step(sh)
     torch.cuda.synchronize()

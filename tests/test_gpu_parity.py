@@ -184,7 +184,9 @@ def test_shared_prefix_equals_private_copies_bitwise():
     shared = Pair(w)
     shared.fill()
     shared.append_step_rows()
-    private = Pair(w)
+    # private copies need room for three full prefixes
+    nb = 4 * w.num_blocks
+    private = Pair(w, free_order=np.random.default_rng(1).permutation(nb), num_blocks=nb)
     for s in range(3):
         private.alloc(s)
         k = np.concatenate([w.prefix_k, w.k_rows[s], w.new_k[s]])
@@ -245,6 +247,7 @@ def test_rollback_then_append():
 def test_nomem_and_invalid_calls_change_nothing():
     w = make_custom(lengths=[20, 20], num_q_heads=4, num_kv_heads=2, head_dim=64, dtype="bf16", seed=33,
                     num_blocks=5)
+    w.max_blocks_per_seq = 8          # long enough that only the pool can run out
     pair = Pair(w)
     pair.fill()
     pair.check_pools_and_tables()
