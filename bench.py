@@ -264,6 +264,7 @@ def main():
     start.record(stream)
     for i in range(args.steps):
         reps[i % len(reps)].step(sh)
+    t_enq = time.perf_counter() - t0
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -301,6 +302,7 @@ def main():
                       "merge": round(1e3 * kern[1][0] / max(1, kern[1][1]), 2) if kern[1][1] else None,
                       "append": round(1e3 * kern[2][0] / max(1, kern[2][1]), 2) if kern[2][1] else None},
         "host_wall_ms_per_step": round(1e3 * wall / args.steps, 4),
+        "host_enqueue_us_per_step": round(1e6 * t_enq / args.steps, 2),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -2,7 +2,6 @@
 #include "block_pool.hpp"
 
 #include <algorithm>
-#include <unordered_map>
 
 namespace pa {
 
@@ -34,8 +33,13 @@ int BlockPool::init(int num_blocks, int max_seqs, int max_blocks_per_seq,
   rc_.assign(num_blocks, 0);
   tables_.assign(max_seqs, {});
   len_.assign(max_seqs, -1);
-  dirty_entries_.clear();
-  dirty_lens_.clear();
+  entry_flag_.assign(static_cast<size_t>(max_seqs) * max_blocks_per_seq, 0);
+  len_flag_.assign(max_seqs, 0);
+  seen_flag_.assign(max_seqs, 0);
+  dirty_entry_list_.clear();
+  dirty_len_list_.clear();
+  rc_delta_.assign(num_blocks, 0);
+  touched_.clear();
   return kOk;
 }
 
@@ -82,23 +86,30 @@ int BlockPool::append(const int32_t* seqs, int n_seq, const int32_t* n_tok,
   if (n_seq > 0 && (!seqs || !n_tok)) return fail(err, kInvalid, "seq_ids / n_tok are NULL");
   // Validate everything first and count the blocks the call needs, following
   // reference counts as earlier sequences of the same call copy shared tails.
-  std::unordered_set<int32_t> uniq;
-  std::unordered_map<int32_t, int32_t> rc_delta;
   int64_t need = 0;
-  for (int i = 0; i < n_seq; ++i) {
+  int bad = kOk;
+  const char* why = nullptr;
+  int i = 0;
+  for (; i < n_seq; ++i) {
     const int s = seqs[i];
-    if (!live(s)) return fail(err, kInvalid, "append to a sequence that is not live");
-    if (!uniq.insert(s).second) return fail(err, kInvalid, "sequence repeated in one append");
-    if (n_tok[i] < 0) return fail(err, kInvalid, "negative token count");
+    if (!live(s)) { bad = kInvalid; why = "append to a sequence that is not live"; break; }
+    if (seen_flag_[s]) { bad = kInvalid; why = "sequence repeated in one append"; break; }
+    seen_flag_[s] = 1;
+    if (n_tok[i] < 0) { ++i; bad = kInvalid; why = "negative token count"; break; }
     const int64_t len = len_[s];
-    if (len + n_tok[i] > static_cast<int64_t>(max_blocks_) * kBlock)
-      return fail(err, kInvalid, "sequence would exceed max_blocks_per_seq");
+    if (len + n_tok[i] > static_cast<int64_t>(max_blocks_) * kBlock) {
+      ++i;
+      bad = kInvalid;
+      why = "sequence would exceed max_blocks_per_seq";
+      break;
+    }
     if (n_tok[i] == 0) continue;
     if (len % kBlock != 0) {
       const int32_t tail = tables_[s].back();
-      if (rc_[tail] + rc_delta[tail] > 1) {
+      if (rc_[tail] + rc_delta_[tail] > 1) {
         ++need;
-        --rc_delta[tail];
+        if (rc_delta_[tail] == 0) touched_.push_back(tail);
+        --rc_delta_[tail];
       }
     }
     // blocks that start inside [len, len + n): positions p with p % 16 == 0
@@ -106,6 +117,12 @@ int BlockPool::append(const int32_t* seqs, int n_seq, const int32_t* n_tok,
     const int64_t last = (len + n_tok[i] - 1) / kBlock;
     need += last - first + 1;
   }
+  // clear the scratch marks whatever the outcome
+  for (int k = 0; k < std::min(i, n_seq); ++k)
+    if (seqs[k] >= 0 && seqs[k] < max_seqs_) seen_flag_[seqs[k]] = 0;
+  for (int32_t b : touched_) rc_delta_[b] = 0;
+  touched_.clear();
+  if (bad != kOk) return fail(err, bad, why);
   if (need > static_cast<int64_t>(free_.size()))
     return fail(err, kNoMem, "not enough free blocks for this append");
 
@@ -159,23 +176,21 @@ void BlockPool::take_dirty(Dirty* out) {
   out->table_val.clear();
   out->len_seq.clear();
   out->len_val.clear();
-  std::vector<int32_t> idx(dirty_entries_.begin(), dirty_entries_.end());
-  std::sort(idx.begin(), idx.end());
-  for (int32_t f : idx) {
+  for (int32_t f : dirty_entry_list_) {
+    entry_flag_[f] = 0;
     const int s = f / max_blocks_;
     const int j = f % max_blocks_;
     if (len_[s] < 0 || j >= static_cast<int>(tables_[s].size())) continue;  // no longer used
     out->table_idx.push_back(f);
     out->table_val.push_back(tables_[s][j]);
   }
-  std::vector<int32_t> ls(dirty_lens_.begin(), dirty_lens_.end());
-  std::sort(ls.begin(), ls.end());
-  for (int32_t s : ls) {
+  for (int32_t s : dirty_len_list_) {
+    len_flag_[s] = 0;
     out->len_seq.push_back(s);
     out->len_val.push_back(len_[s] < 0 ? 0 : len_[s]);
   }
-  dirty_entries_.clear();
-  dirty_lens_.clear();
+  dirty_entry_list_.clear();
+  dirty_len_list_.clear();
 }
 
 }  // namespace pa

@@ -18,7 +18,6 @@
 #include <cstdint>
 #include <deque>
 #include <string>
-#include <unordered_set>
 #include <vector>
 
 namespace pa {
@@ -56,22 +55,36 @@ class BlockPool {
   int max_seqs() const { return max_seqs_; }
   int max_blocks_per_seq() const { return max_blocks_; }
 
-  // Device-mirror bookkeeping: entries (seq * max_blocks + j) and sequences
-  // whose device copy is stale.  take_dirty() returns them and clears the sets.
+  // Device-mirror bookkeeping: table entries (seq * max_blocks + j) and
+  // sequences whose device copy is stale.  take_dirty() returns them and clears
+  // the marks.  Flags plus lists keep marking and collecting O(1) per item.
   struct Dirty {
     std::vector<int32_t> table_idx;    // flat indices into the device table
     std::vector<int32_t> table_val;    // their current values
     std::vector<int32_t> len_seq;      // sequences whose length changed
     std::vector<int32_t> len_val;      // current length (0 if not live)
   };
-  bool has_dirty() const { return !dirty_entries_.empty() || !dirty_lens_.empty(); }
+  bool has_dirty() const { return !dirty_entry_list_.empty() || !dirty_len_list_.empty(); }
   void take_dirty(Dirty* out);
+  size_t dirty_entries() const { return dirty_entry_list_.size(); }
+  size_t dirty_lens() const { return dirty_len_list_.size(); }
 
  private:
   int32_t pop();
   void release(int32_t b);
-  void mark_entry(int seq, int j) { dirty_entries_.insert(seq * max_blocks_ + j); }
-  void mark_len(int seq) { dirty_lens_.insert(seq); }
+  void mark_entry(int seq, int j) {
+    const int32_t f = seq * max_blocks_ + j;
+    if (!entry_flag_[f]) {
+      entry_flag_[f] = 1;
+      dirty_entry_list_.push_back(f);
+    }
+  }
+  void mark_len(int seq) {
+    if (!len_flag_[seq]) {
+      len_flag_[seq] = 1;
+      dirty_len_list_.push_back(seq);
+    }
+  }
 
   int num_blocks_ = 0;
   int max_seqs_ = 0;
@@ -80,8 +93,9 @@ class BlockPool {
   std::vector<int32_t> rc_;
   std::vector<std::vector<int32_t>> tables_;
   std::vector<int32_t> len_;  // -1 = not live
-  std::unordered_set<int32_t> dirty_entries_;
-  std::unordered_set<int32_t> dirty_lens_;
+  std::vector<uint8_t> entry_flag_, len_flag_, seen_flag_;
+  std::vector<int32_t> dirty_entry_list_, dirty_len_list_;
+  std::vector<int32_t> rc_delta_, touched_;
 };
 
 }  // namespace pa

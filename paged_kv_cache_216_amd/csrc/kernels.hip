@@ -6,7 +6,10 @@
 //  attn_kernel       decode / speculative-verify attention over the block table:
 //                    one 64-lane wave per (sequence, partition, key/value head);
 //                    QK^T and PV on the matrix cores, online softmax in fp32.
-//  merge_kernel      exact log-sum-exp merge of split-context partials.
+//  merge_kernel      exact log-sum-exp merge of the partitions of split
+//                    contexts (a separate launch: on MI355X each XCD has its
+//                    own L2, so merging inside the attention launch would need
+//                    device-scope write-back/invalidate fences per partition).
 //
 // The pages describe the method (16-token blocks reached through a table inside
 // the attention kernel: "PagedAttention, décodage spéculatif, MoE et Blackwell",
@@ -182,6 +185,13 @@ __device__ inline float shfl_f(float x, int src_lane) {
 
 __device__ inline int readlane(int x, int lane) { return __builtin_amdgcn_readlane(x, lane); }
 
+// K/V pages are read once per launch: load them with the non-temporal hint so
+// they stream past the caches instead of evicting the tables and queries.
+template <typename V>
+__device__ inline V stream_load(const V* p) {
+  return __builtin_nontemporal_load(p);
+}
+
 // zero the 16-bit elements of an 8-byte V fragment whose token position >= n
 __device__ inline u32x2 mask_v16(u32x2 v, int pos0, int n) {
   u32x2 r;
@@ -206,9 +216,14 @@ __device__ inline void store_elem(T* p, float v) {
   *p = static_cast<T>(v);
 }
 
+// A work unit with its token range resolved against the current length.
+struct Unit {
+  int q_row, seq, n, tok_begin, tok_end, slot_base, nparts, part;
+};
+
 // 16-bit element types: bf16 or f16
 template <typename T, int D, int NT>
-__device__ inline void attn_body16(const AttnParams& p, const WorkUnit& u, int kvh) {
+__device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) {
   using Op = typename MfmaOp<T>::type;
   constexpr int KS = D / 32;  // QK k-steps per block
   constexpr int DC = D / 16;  // output dim chunks
@@ -257,59 +272,56 @@ __device__ inline void attn_body16(const AttnParams& p, const WorkUnit& u, int k
   const int nblk = (u.tok_end + kBlk - 1) / kBlk - jb0;
   const int mask_from = u.n - p.k_draft;  // positions above this may be masked for some row
 
+  // One pair of blocks = one PV step.  The loads of pair j+1 are issued before
+  // pair j is computed, so each wave keeps 16-32 KiB of K/V in flight (except
+  // for the largest query tiles, whose accumulators need those registers).
+  struct Frag {
+    Op k0[KS], k1[KS];
+    u32x2 v0[DC], v1[DC];
+  };
   for (int cb = 0; cb < nblk; cb += 64) {
     const int cnt = min(64, nblk - cb);
     const int tb = (lane < cnt) ? bt[jb0 + cb + lane] : 0;  // this chunk of the table, one entry per lane
-    for (int j = 0; j < cnt; j += 2) {
-      const bool has1 = (j + 1) < cnt;
-      // a table entry outside the pool can only come from a host-side bug; clamp
-      // it so that the bug shows as a wrong result, never as a stray access
-      const int phys0 = min(max(readlane(tb, j), 0), p.num_blocks - 1);
-      const int phys1 = min(max(readlane(tb, min(j + 1, 63)), 0), p.num_blocks - 1);
-      const int pos0 = (jb0 + cb + j) * kBlk;  // first token of the pair
+    const int npairs = (cnt + 1) >> 1;
+    // a table entry outside the pool can only come from a host-side bug; clamp
+    // it so that the bug shows as a wrong result, never as a stray access
+    auto phys_at = [&](int j) { return min(max(readlane(tb, j), 0), p.num_blocks - 1); };
+    // Branch-free: a pair past the end (or the missing second block of an odd
+    // count) re-reads blocks already requested, which hit in cache, and every
+    // position it contributes is masked.  Uniform control flow lets the
+    // compiler wait only for the pair being computed.
+    auto load = [&](Frag& f, int pj) {
+      const int j = min(2 * pj, cnt - 1);
+      const int phys0 = phys_at(j);
+      const int phys1 = phys_at(min(j + 1, cnt - 1));
       const T* kp0 = kpool + (static_cast<size_t>(phys0) * p.hkv + kvh) * page;
       const T* vp0 = vpool + (static_cast<size_t>(phys0) * p.hkv + kvh) * page;
       const T* kp1 = kpool + (static_cast<size_t>(phys1) * p.hkv + kvh) * page;
       const T* vp1 = vpool + (static_cast<size_t>(phys1) * p.hkv + kvh) * page;
-
-      Op k0[KS], k1[KS];
-      u32x2 v0[DC], v1[DC];
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        k0[s] = __builtin_bit_cast(Op, *reinterpret_cast<const u32x4*>(kp0 + ((4 * s + grp) * kBlk + col) * 8));
+        f.k0[s] = __builtin_bit_cast(Op, stream_load(reinterpret_cast<const u32x4*>(kp0 + ((4 * s + grp) * kBlk + col) * 8)));
 #pragma unroll
-      for (int c = 0; c < DC; ++c)
-        v0[c] = *reinterpret_cast<const u32x2*>(vp0 + (16 * c + col) * kBlk + 4 * grp);
-      if (has1) {
+      for (int s = 0; s < KS; ++s)
+        f.k1[s] = __builtin_bit_cast(Op, stream_load(reinterpret_cast<const u32x4*>(kp1 + ((4 * s + grp) * kBlk + col) * 8)));
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-          k1[s] = __builtin_bit_cast(Op, *reinterpret_cast<const u32x4*>(kp1 + ((4 * s + grp) * kBlk + col) * 8));
+      for (int c = 0; c < DC; ++c) f.v0[c] = stream_load(reinterpret_cast<const u32x2*>(vp0 + (16 * c + col) * kBlk + 4 * grp));
 #pragma unroll
-        for (int c = 0; c < DC; ++c)
-          v1[c] = *reinterpret_cast<const u32x2*>(vp1 + (16 * c + col) * kBlk + 4 * grp);
-      } else {
-#pragma unroll
-        for (int s = 0; s < KS; ++s) k1[s] = Op{};
-#pragma unroll
-        for (int c = 0; c < DC; ++c) v1[c] = u32x2{0u, 0u};
-      }
-      // slots past the end of the sequence may hold anything: zero their V
-      if (pos0 + 2 * kBlk > u.n) {
-#pragma unroll
-        for (int c = 0; c < DC; ++c) {
-          v0[c] = mask_v16(v0[c], pos0 + 4 * grp, u.n);
-          v1[c] = mask_v16(v1[c], pos0 + kBlk + 4 * grp, u.n);
-        }
-      }
+      for (int c = 0; c < DC; ++c) f.v1[c] = stream_load(reinterpret_cast<const u32x2*>(vp1 + (16 * c + col) * kBlk + 4 * grp));
+    };
+    auto process = [&](Frag& f, int pj) {
+      const int pos0 = (jb0 + cb + 2 * pj) * kBlk;  // first token of the pair
       const bool need_mask = (pos0 + 2 * kBlk - 1 > mask_from) || (pos0 + 2 * kBlk > u.tok_end);
-
+      Op pa[NT];
+      float a4[NT][4];
+      // scores and online-softmax update for every row tile (needs K only)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          s0 = MfmaOp<T>::mma(k0[s], qop[nt][s], s0);
-          s1 = MfmaOp<T>::mma(k1[s], qop[nt][s], s1);
+          s0 = MfmaOp<T>::mma(f.k0[s], qop[nt][s], s0);
+          s1 = MfmaOp<T>::mma(f.k1[s], qop[nt][s], s1);
         }
         float x[8];
 #pragma unroll
@@ -333,26 +345,54 @@ __device__ inline void attn_body16(const AttnParams& p, const WorkUnit& u, int k
         const float m_use = (m_new == kNegInf) ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
         float ps = 0.f;
-        Op pa;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float pe = __builtin_amdgcn_exp2f(x[e] - m_use);
           ps += pe;
-          pa[e] = static_cast<T>(pe);
+          pa[nt][e] = static_cast<T>(pe);
         }
         l_run[nt] = l_run[nt] * alpha + ps;
         m_run[nt] = m_new;
-        // rescale accumulators: lane holds rows 4*grp + jj
-        float a4[4];
+        // rescale factors move to the accumulator layout: lane holds rows 4*grp + jj
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) a4[jj] = shfl_f(alpha, 4 * grp + jj);
+        for (int jj = 0; jj < 4; ++jj) a4[nt][jj] = shfl_f(alpha, 4 * grp + jj);
+      }
+      // slots past the end of the sequence may hold anything: zero their V
+      if (pos0 + 2 * kBlk > u.n) {
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          f.v0[c] = mask_v16(f.v0[c], pos0 + 4 * grp, u.n);
+          f.v1[c] = mask_v16(f.v1[c], pos0 + kBlk + 4 * grp, u.n);
+        }
+      }
+      // O = diag(alpha) O + P V
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) acc[nt][c][jj] *= a4[jj];
-          const Op vb = __builtin_bit_cast(Op, u32x4{v0[c][0], v0[c][1], v1[c][0], v1[c][1]});
-          acc[nt][c] = MfmaOp<T>::mma(pa, vb, acc[nt][c]);
+          for (int jj = 0; jj < 4; ++jj) acc[nt][c][jj] *= a4[nt][jj];
+          const Op vb = __builtin_bit_cast(Op, u32x4{f.v0[c][0], f.v0[c][1], f.v1[c][0], f.v1[c][1]});
+          acc[nt][c] = MfmaOp<T>::mma(pa[nt], vb, acc[nt][c]);
         }
+      }
+    };
+    if constexpr (D * NT < 512) {
+      Frag fa, fb;
+      load(fa, 0);
+      for (int pj = 0; pj < npairs; pj += 2) {
+        load(fb, min(pj + 1, npairs - 1));
+        process(fa, pj);
+        if (pj + 1 >= npairs) break;
+        load(fa, min(pj + 2, npairs - 1));
+        process(fb, pj + 1);
+      }
+    } else {
+      // the largest query tiles leave no registers for a second pair in flight
+      for (int pj = 0; pj < npairs; ++pj) {
+        Frag fa;
+        load(fa, pj);
+        process(fa, pj);
       }
     }
   }
@@ -405,7 +445,7 @@ __device__ inline void attn_body16(const AttnParams& p, const WorkUnit& u, int k
 
 // fp32 elements: v_mfma_f32_16x16x4_f32 (one dim per lane per instruction)
 template <int D, int NT>
-__device__ inline void attn_body32(const AttnParams& p, const WorkUnit& u, int kvh) {
+__device__ inline void attn_body32(const AttnParams& p, const Unit& u, int kvh) {
   constexpr int KS = D / 16;  // 16-byte K chunks per lane per block
   constexpr int DC = D / 16;
   const int lane = threadIdx.x;
@@ -562,39 +602,94 @@ template <typename T, int D, int NT>
 __global__ __launch_bounds__(64) void attn_kernel(AttnParams p) {
   const int unit = blockIdx.x / p.hkv;
   const int kvh = blockIdx.x - unit * p.hkv;
-  const WorkUnit u = p.units[unit];
+  const WorkUnit w = p.units[unit];
+  Unit u;
+  u.q_row = w.q_row;
+  u.seq = w.seq;
+  u.slot_base = w.slot_base;
+  u.nparts = w.nparts;
+  u.part = w.part;
+  // the length mirror is bounded by the table row the host allocated
+  u.n = min(p.seq_len[w.seq], p.max_blocks * kBlk);
+  u.tok_begin = w.nparts > 1 ? w.part * p.part_tokens : 0;
+  u.tok_end = w.nparts > 1 ? min(u.n, u.tok_begin + p.part_tokens) : u.n;
   if constexpr (std::is_same_v<T, float>)
     attn_body32<D, NT>(p, u, kvh);
   else
     attn_body16<T, D, NT>(p, u, kvh);
 }
 
-// exact merge of partials: O = sum_p w_p acc_p / sum_p w_p l_p, w_p = 2^(m_p - M)
-template <typename T>
-__global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
-  const int mu_idx = blockIdx.x / p.hkv;
-  const int kvh = blockIdx.x - mu_idx * p.hkv;
-  const MergeUnit mu = p.merges[mu_idx];
-  const int D = p.head_dim;
+// Exact merge of one output row of a split sequence, one 256-thread workgroup
+// per (sequence, key/value head, query row):
+//   M = max_p m_p,  w_p = 2^(m_p - M),  O = sum_p w_p acc_p / sum_p w_p l_p,
+//   lse = (M + log2 sum_p w_p l_p) * ln 2
+// The D/4 16-byte chunks of a row are spread over D/4 threads; the partitions
+// over NG = 1024/D groups of such threads (partition q to group q % NG), so
+// every thread has several independent loads in flight.  Groups are combined
+// in a fixed order, so the result is deterministic.
+constexpr int kMergeThreads = 256;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
+  constexpr int NC = D / 4;                 // float4 chunks per row
+  constexpr int NG = kMergeThreads / NC;    // partition groups
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ f32x4 part_acc[NG][NC];
+  __shared__ float part_den[NG];
+  const int tid = threadIdx.x;
   const int rows = p.rows;
-  const int G = p.group;
-  const int base = mu.slot_base + kvh * mu.nparts;
-  for (int e = threadIdx.x; e < rows * D; e += blockDim.x) {
-    const int r = e / D;
-    const int d = e - r * D;
-    float M = kNegInf;
-    for (int q = 0; q < mu.nparts; ++q) M = fmaxf(M, p.ws_ml[(static_cast<size_t>(base + q) * rows + r) * 2]);
-    float den = 0.f, num = 0.f;
-    for (int q = 0; q < mu.nparts; ++q) {
-      const size_t s = static_cast<size_t>(base + q) * rows + r;
-      const float w = __builtin_amdgcn_exp2f(p.ws_ml[s * 2] - M);
-      den += p.ws_ml[s * 2 + 1] * w;
-      num += p.ws_acc[s * D + d] * w;
+  const int r = blockIdx.x % rows;
+  const int rest = blockIdx.x / rows;
+  const int kvh = rest % p.hkv;
+  const MergeUnit mu = p.merges[rest / p.hkv];
+  const int P = mu.nparts;
+  const int base = mu.slot_base + kvh * P;
+  const float* ml = p.ws_ml + (static_cast<size_t>(base) * rows + r) * 2;  // partition q at ml[q * rows * 2]
+  const size_t mstride = static_cast<size_t>(rows) * 2;
+  // block-wide max of m_q
+  float M = kNegInf;
+  for (int q = tid; q < P; q += kMergeThreads) M = fmaxf(M, ml[q * mstride]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if ((tid & 63) == 0) red[tid >> 6] = M;
+  __syncthreads();
+  M = red[0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, red[w]);
+  // weighted sums: thread (g, c) takes chunk c of partitions g, g + NG, ...
+  const int g = tid / NC;
+  const int c = tid - g * NC;
+  const f32x4* acc = reinterpret_cast<const f32x4*>(p.ws_acc + (static_cast<size_t>(base) * rows + r) * D) + c;
+  const size_t astride = static_cast<size_t>(rows) * D / 4;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+#pragma unroll 8
+  for (int q = g; q < P; q += NG) {
+    const float w = __builtin_amdgcn_exp2f(ml[q * mstride] - M);
+    den += w * ml[q * mstride + 1];
+    const f32x4 a = acc[q * astride];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) num[e] += w * a[e];
+  }
+  part_acc[g][c] = num;
+  if (c == 0) part_den[g] = den;
+  __syncthreads();
+  if (tid < NC) {
+    f32x4 sum = part_acc[0][tid];
+    float dsum = part_den[0];
+#pragma unroll
+    for (int k = 1; k < NG; ++k) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sum[e] += part_acc[k][tid][e];
+      dsum += part_den[k];
     }
-    const int i = r / G, g = r - (r / G) * G;
-    const size_t orow = static_cast<size_t>(mu.q_row * p.k_draft + i) * p.hq + kvh * G + g;
-    store_elem(static_cast<T*>(p.out) + orow * D + d, num / den);
-    if (d == 0 && p.lse) p.lse[orow] = (M + __builtin_amdgcn_logf(den)) * kLn2;
+    const int i = r / p.group, gg = r - (r / p.group) * p.group;
+    const size_t orow = static_cast<size_t>(mu.q_row * p.k_draft + i) * p.hq + kvh * p.group + gg;
+    const float inv = 1.f / dsum;
+    T* op = static_cast<T*>(p.out) + orow * D + 4 * tid;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_elem(op + e, sum[e] * inv);
+    if (tid == 0 && p.lse) p.lse[orow] = (M + __builtin_amdgcn_logf(dsum)) * kLn2;
   }
 }
 
@@ -639,6 +734,29 @@ hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_merge_t(const AttnParams& p, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(p.n_merges) * p.hkv * p.rows);
+  const dim3 block(kMergeThreads);
+  switch (p.head_dim) {
+    case 64: hipLaunchKernelGGL((merge_kernel<T, 64>), grid, block, 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((merge_kernel<T, 128>), grid, block, 0, stream, p); break;
+    case 256: hipLaunchKernelGGL((merge_kernel<T, 256>), grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(DType dt, const AttnParams& p, hipStream_t stream) {
+  if (p.n_merges == 0) return hipSuccess;
+  switch (dt) {
+    case kBF16: return launch_merge_t<__bf16>(p, stream);
+    case kF16: return launch_merge_t<_Float16>(p, stream);
+    case kF32: return launch_merge_t<float>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_attention(DType dt, const AttnParams& p, hipStream_t stream) {
   if (p.n_units == 0) return hipSuccess;
   switch (dt) {
@@ -647,17 +765,6 @@ hipError_t launch_attention(DType dt, const AttnParams& p, hipStream_t stream) {
     case kF32: return launch_attn_t<float>(p, stream);
   }
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_merge(DType dt, const AttnParams& p, hipStream_t stream) {
-  if (p.n_merges == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(p.n_merges) * p.hkv);
-  switch (dt) {
-    case kBF16: hipLaunchKernelGGL((merge_kernel<__bf16>), grid, dim3(256), 0, stream, p); break;
-    case kF16: hipLaunchKernelGGL((merge_kernel<_Float16>), grid, dim3(256), 0, stream, p); break;
-    case kF32: hipLaunchKernelGGL((merge_kernel<float>), grid, dim3(256), 0, stream, p); break;
-  }
-  return hipGetLastError();
 }
 
 }  // namespace pa

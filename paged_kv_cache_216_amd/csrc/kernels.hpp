@@ -11,7 +11,8 @@ namespace pa {
 enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
 // One launch applies pending device-table updates, copy-on-write block copies
-// and the scatter of new rows.  Metadata (int32) lives in one device buffer:
+// and the scatter of new rows.  The int32 metadata is read by the kernel
+// straight from pinned host memory:
 //   tab  [n_tab][2]  (flat table index, physical block)
 //   lens [n_len][2]  (sequence, length)
 //   cows [n_cow][3]  (src block, dst block, rows to copy)
@@ -32,18 +33,19 @@ struct AppendParams {
 };
 
 // Work unit of the attention kernel, one per (sequence, partition); the
-// key/value head comes from the grid.
+// key/value head comes from the grid.  Lengths are not part of the unit: the
+// kernel reads them from the device length mirror, so a plan stays valid while
+// sequences grow inside their partitions.
 struct WorkUnit {
   int32_t q_row;      // index of the sequence in q / out (0..n_seq-1)
-  int32_t seq;        // row of the block table
-  int32_t n;          // tokens in the sequence
-  int32_t tok_begin;  // first token of this partition (multiple of 32)
-  int32_t tok_end;    // one past the last token of this partition
+  int32_t seq;        // row of the block table and of the length mirror
+  int32_t part;       // partition index
+  int32_t nparts;     // partitions of this sequence (1 = unsplit)
   int32_t slot_base;  // -1: write out/lse directly; else partial slot of kv head 0, part 0
-  int32_t nparts;     // partitions of this sequence
-  int32_t part;       // this unit's partition index
+  int32_t pad0, pad1, pad2;
 };
 
+// One split sequence: its partials are merged into out / lse.
 struct MergeUnit {
   int32_t q_row;
   int32_t slot_base;
@@ -55,8 +57,10 @@ struct AttnParams {
   const void* k_pool;
   const void* v_pool;
   const int32_t* block_table;
+  const int32_t* seq_len;
   int max_blocks;
   int num_blocks;     // physical blocks; table entries are clamped into range
+  int part_tokens;    // partition length of split sequences (multiple of 32)
   const void* q;
   void* out;
   float* lse;
@@ -72,7 +76,6 @@ struct AttnParams {
 };
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
-// kernel_ms_event_*: optional events recorded around the attention launch
 hipError_t launch_attention(DType dt, const AttnParams& p, hipStream_t stream);
 hipError_t launch_merge(DType dt, const AttnParams& p, hipStream_t stream);
 // Largest supported rows (group * k_draft) for a head dim.

@@ -1,6 +1,14 @@
-// C-ABI entry points declared in include/pa.h.  Host-side validation, the block
-// allocator, packing of per-call metadata into one pinned buffer, a single
-// host-to-device copy of it, and the kernel launches.
+// C-ABI entry points declared in include/pa.h.
+//
+// Host side of every device call: validate, update the block allocator, write
+// the call's per-call metadata (table updates, copies, slots) into one pinned,
+// device-visible host buffer, and launch the kernels, which read that buffer
+// directly -- no separate host-to-device copy is enqueued.  A ring of such
+// buffers, each released by an event recorded after the last kernel that reads
+// it, lets the host run ahead of the GPU.  The attention work plan (which
+// sequence / partition each workgroup takes) lives in device memory and is
+// re-uploaded only when the batch or its partition structure changes; lengths
+// come from the device length mirror.
 #include "../../include/pa.h"
 
 #include <hip/hip_runtime.h>
@@ -8,7 +16,6 @@
 #include <algorithm>
 #include <cstring>
 #include <new>
-#include <numeric>
 #include <string>
 #include <vector>
 
@@ -28,12 +35,13 @@ int hip_err(hipError_t e, const char* what) {
   return set_err(PA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-constexpr int kStages = 4;
+constexpr int kStages = 64;
 constexpr int kDefaultPartition = 512;
 
 struct Stage {
-  int32_t* host = nullptr;  // pinned
-  size_t cap = 0;           // bytes
+  int32_t* host = nullptr;  // pinned, fine-grained (the GPU reads it without caching it)
+  int32_t* dev = nullptr;   // the same memory as seen by the GPU
+  size_t cap = 0;           // int32 words
   hipEvent_t done = nullptr;
   bool pending = false;
 };
@@ -45,6 +53,8 @@ struct ProfEvent {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+size_t pad8(size_t n) { return (n + 7) & ~size_t(7); }
+
 }  // namespace
 
 struct pa_pool {
@@ -55,11 +65,22 @@ struct pa_pool {
   int32_t* block_table = nullptr;
   int32_t* seq_len = nullptr;
   bool host_only = false;
-  // metadata buffers
-  int32_t* dmeta = nullptr;
-  size_t dmeta_cap = 0;
+  // metadata ring
   Stage stage[kStages];
   int next_stage = 0;
+  // cached attention plan in device memory: WorkUnits then MergeUnits
+  void* dplan = nullptr;
+  size_t dplan_cap = 0;  // bytes
+  std::vector<int32_t> plan_key, key_scratch;
+  int plan_units = 0, plan_merges = 0;
+  int64_t plan_slots = 0;
+  // reused host scratch
+  pa::BlockPool::Dirty dirty;
+  std::vector<int32_t> slots;
+  std::vector<pa::CowCopy> cows;
+  std::vector<pa::WorkUnit> units, tail_units;
+  std::vector<pa::MergeUnit> merges;
+  std::vector<int> lens, parts;
   // profiling
   bool prof = false;
   std::vector<ProfEvent> prof_events;
@@ -69,35 +90,8 @@ struct pa_pool {
 
 namespace {
 
-// Grow-only buffers.  A larger device buffer is only swapped in after the
-// device is idle, so in-flight kernels never read freed memory.
-int ensure_capacity(pa_pool* p, Stage& st, size_t bytes) {
-  if (bytes > p->dmeta_cap) {
-    size_t cap = std::max<size_t>(bytes, 2 * p->dmeta_cap);
-    hipError_t e = hipDeviceSynchronize();
-    if (e != hipSuccess) return hip_err(e, "hipDeviceSynchronize");
-    if (p->dmeta) hipFree(p->dmeta);
-    p->dmeta = nullptr;
-    p->dmeta_cap = 0;
-    e = hipMalloc(&p->dmeta, cap);
-    if (e != hipSuccess) return hip_err(e, "hipMalloc(metadata)");
-    p->dmeta_cap = cap;
-  }
-  if (bytes > st.cap) {
-    size_t cap = std::max<size_t>(bytes, 2 * st.cap);
-    if (st.host) hipHostFree(st.host);
-    st.host = nullptr;
-    st.cap = 0;
-    hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&st.host), cap, hipHostMallocDefault);
-    if (e != hipSuccess) return hip_err(e, "hipHostMalloc(staging)");
-    st.cap = cap;
-  }
-  return PA_OK;
-}
-
-// Copy `words` to the device metadata buffer on `stream`.
-int upload(pa_pool* p, const std::vector<int32_t>& words, hipStream_t stream) {
-  if (words.empty()) return PA_OK;
+// Take the next ring buffer with room for `words` int32 values.
+int acquire_stage(pa_pool* p, size_t words, Stage** out) {
   Stage& st = p->stage[p->next_stage];
   p->next_stage = (p->next_stage + 1) % kStages;
   if (st.pending) {
@@ -105,22 +99,42 @@ int upload(pa_pool* p, const std::vector<int32_t>& words, hipStream_t stream) {
     if (e != hipSuccess) return hip_err(e, "hipEventSynchronize(staging)");
     st.pending = false;
   }
-  const size_t bytes = words.size() * sizeof(int32_t);
-  int rc = ensure_capacity(p, st, bytes);
-  if (rc != PA_OK) return rc;
-  std::memcpy(st.host, words.data(), bytes);
-  hipError_t e = hipMemcpyAsync(p->dmeta, st.host, bytes, hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync(metadata)");
-  e = hipEventRecord(st.done, stream);
-  if (e != hipSuccess) return hip_err(e, "hipEventRecord(staging)");
-  st.pending = true;
+  if (words > st.cap) {
+    const size_t cap = std::max<size_t>(words, std::max<size_t>(2 * st.cap, 4096));
+    if (st.host) hipHostFree(st.host);
+    st.host = st.dev = nullptr;
+    st.cap = 0;
+    hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&st.host), cap * sizeof(int32_t),
+                                 hipHostMallocCoherent | hipHostMallocMapped);
+    if (e != hipSuccess) return hip_err(e, "hipHostMalloc(staging)");
+    e = hipHostGetDevicePointer(reinterpret_cast<void**>(&st.dev), st.host, 0);
+    if (e != hipSuccess) return hip_err(e, "hipHostGetDevicePointer(staging)");
+    st.cap = cap;
+  }
+  *out = &st;
   return PA_OK;
 }
 
-// Section offsets are kept at multiples of 8 words (32 bytes).
-size_t pad8(std::vector<int32_t>& w) {
-  while (w.size() % 8) w.push_back(0);
-  return w.size();
+// The buffer may be rewritten once the work enqueued so far on `stream` is done.
+int release_stage(Stage* st, hipStream_t stream) {
+  hipError_t e = hipEventRecord(st->done, stream);
+  if (e != hipSuccess) return hip_err(e, "hipEventRecord(staging)");
+  st->pending = true;
+  return PA_OK;
+}
+
+int ensure_dplan(pa_pool* p, size_t bytes) {
+  if (bytes <= p->dplan_cap) return PA_OK;
+  const size_t cap = std::max(bytes, 2 * p->dplan_cap);
+  hipError_t e = hipDeviceSynchronize();  // no launch may still read the old plan
+  if (e != hipSuccess) return hip_err(e, "hipDeviceSynchronize");
+  if (p->dplan) hipFree(p->dplan);
+  p->dplan = nullptr;
+  p->dplan_cap = 0;
+  e = hipMalloc(&p->dplan, cap);
+  if (e != hipSuccess) return hip_err(e, "hipMalloc(plan)");
+  p->dplan_cap = cap;
+  return PA_OK;
 }
 
 void prof_begin(pa_pool* p, int which, hipStream_t s, ProfEvent* ev) {
@@ -137,25 +151,6 @@ void prof_end(pa_pool* p, hipStream_t s, ProfEvent* ev) {
   p->prof_events.push_back(*ev);
 }
 
-// Pending table / length updates, appended to `w`; counts returned.
-void pack_dirty(pa_pool* p, std::vector<int32_t>& w, int* n_tab, int* n_len, size_t* tab_off,
-                size_t* len_off) {
-  pa::BlockPool::Dirty d;
-  p->bp.take_dirty(&d);
-  *tab_off = pad8(w);
-  for (size_t i = 0; i < d.table_idx.size(); ++i) {
-    w.push_back(d.table_idx[i]);
-    w.push_back(d.table_val[i]);
-  }
-  *len_off = pad8(w);
-  for (size_t i = 0; i < d.len_seq.size(); ++i) {
-    w.push_back(d.len_seq[i]);
-    w.push_back(d.len_val[i]);
-  }
-  *n_tab = static_cast<int>(d.table_idx.size());
-  *n_len = static_cast<int>(d.len_seq.size());
-}
-
 pa::AppendParams base_append(pa_pool* p) {
   pa::AppendParams ap{};
   ap.k_pool = p->k_pool;
@@ -168,36 +163,77 @@ pa::AppendParams base_append(pa_pool* p) {
   return ap;
 }
 
+// Write the pending table / length updates at host[*off]; fills ap.
+void write_dirty(pa_pool* p, int32_t* host, int32_t* dev, size_t* off, pa::AppendParams* ap) {
+  const pa::BlockPool::Dirty& d = p->dirty;
+  size_t o = *off;
+  ap->tab = dev + o;
+  for (size_t i = 0; i < d.table_idx.size(); ++i) {
+    host[o++] = d.table_idx[i];
+    host[o++] = d.table_val[i];
+  }
+  o = pad8(o);
+  ap->lens = dev + o;
+  for (size_t i = 0; i < d.len_seq.size(); ++i) {
+    host[o++] = d.len_seq[i];
+    host[o++] = d.len_val[i];
+  }
+  o = pad8(o);
+  ap->n_tab = static_cast<int>(d.table_idx.size());
+  ap->n_len = static_cast<int>(d.len_seq.size());
+  *off = o;
+}
+
+size_t dirty_words(const pa_pool* p) {
+  return pad8(2 * p->dirty.table_idx.size()) + pad8(2 * p->dirty.len_seq.size());
+}
+
 int rows_limit(const pa_pool* p) { return pa::max_rows_for_head_dim(p->head_dim); }
 
-// Work decomposition shared by pa_decode / pa_verify / pa_workspace_size.
-struct Plan {
-  std::vector<pa::WorkUnit> units;
-  std::vector<pa::MergeUnit> merges;
+// Partitions per sequence for partition length pt (0 = no split); returns the
+// number of partial slots (kv heads x partitions of every split sequence).
+int64_t count_parts(pa_pool* p, int n_seq, int pt) {
+  p->parts.resize(n_seq);
   int64_t slots = 0;
-};
-
-void make_plan(const pa_pool* p, const int32_t* seq_ids, const int* lens, int n_seq, int pt, Plan* out) {
-  out->units.clear();
-  out->merges.clear();
-  out->slots = 0;
   for (int i = 0; i < n_seq; ++i) {
-    const int n = lens[i];
-    const int parts = (pt > 0 && n > pt) ? (n + pt - 1) / pt : 1;
+    const int n = p->lens[i];
+    p->parts[i] = (pt > 0 && n > pt) ? (n + pt - 1) / pt : 1;
+    if (p->parts[i] > 1) slots += static_cast<int64_t>(p->parts[i]) * p->hkv;
+  }
+  return slots;
+}
+
+// Work decomposition: one unit per (sequence, partition); units of split
+// sequences get consecutive partial slots (kv head major within a sequence).
+// Full-length units first, then the rest longest first (by the lengths at plan
+// time), so the grid's tail holds the short ones.
+void make_plan(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt) {
+  std::vector<pa::WorkUnit>& units = p->units;
+  std::vector<pa::WorkUnit>& tail = p->tail_units;
+  units.clear();
+  tail.clear();
+  p->merges.clear();
+  int64_t slots = 0;
+  for (int i = 0; i < n_seq; ++i) {
+    const int parts = p->parts[i];
     if (parts == 1) {
-      out->units.push_back({i, seq_ids[i], n, 0, n, -1, 1, 0});
+      tail.push_back({i, seq_ids[i], 0, 1, -1, p->lens[i], 0, 0});
       continue;
     }
-    const int base = static_cast<int>(out->slots);
-    out->slots += static_cast<int64_t>(parts) * p->hkv;
-    for (int q = 0; q < parts; ++q)
-      out->units.push_back({i, seq_ids[i], n, q * pt, std::min(n, (q + 1) * pt), base, parts, q});
-    out->merges.push_back({i, base, parts, 0});
+    const int base = static_cast<int>(slots);
+    slots += static_cast<int64_t>(parts) * p->hkv;
+    for (int q = 0; q < parts; ++q) {
+      const int len = std::min(p->lens[i], (q + 1) * pt) - q * pt;
+      (len == pt ? units : tail).push_back({i, seq_ids[i], q, parts, base, len, 0, 0});
+    }
+    p->merges.push_back({i, base, parts, 0});
   }
-  // longest units first, so the tail of the grid holds the short ones
-  std::stable_sort(out->units.begin(), out->units.end(), [](const pa::WorkUnit& a, const pa::WorkUnit& b) {
-    return (a.tok_end - a.tok_begin) > (b.tok_end - b.tok_begin);
+  // pad0 holds the unit's length at plan time, used only for this ordering
+  std::sort(tail.begin(), tail.end(), [](const pa::WorkUnit& a, const pa::WorkUnit& b) {
+    return a.pad0 != b.pad0 ? a.pad0 > b.pad0 : (a.q_row != b.q_row ? a.q_row < b.q_row : a.part < b.part);
   });
+  units.insert(units.end(), tail.begin(), tail.end());
+  p->plan_slots = slots;
 }
 
 size_t plan_ws_bytes(const pa_pool* p, int64_t slots, int rows) {
@@ -223,100 +259,113 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   if (n_seq > 0 && (!seq_ids || !q || !out)) return set_err(PA_ERR_INVALID, "seq_ids, q or out is NULL");
   if (!aligned16(q) || !aligned16(out) || !aligned16(workspace))
     return set_err(PA_ERR_INVALID, "q, out and workspace must be 16-byte aligned");
-  std::vector<int> lens(n_seq);
-  int max_len = 0;
+  p->lens.resize(n_seq);
   for (int i = 0; i < n_seq; ++i) {
     const int s = seq_ids[i];
     if (!p->bp.live(s)) return set_err(PA_ERR_INVALID, "attention over a sequence that is not live");
-    lens[i] = p->bp.length(s);
-    if (lens[i] < std::max(1, k_draft))
+    p->lens[i] = p->bp.length(s);
+    if (p->lens[i] < std::max(1, k_draft))
       return set_err(PA_ERR_INVALID, "sequence shorter than max(1, k_draft)");
-    max_len = std::max(max_len, lens[i]);
   }
   int pt = partition_tokens;
-  Plan plan;
+  int64_t slots;
   if (pt == 0) {
     pt = kDefaultPartition;
-    make_plan(p, seq_ids, lens.data(), n_seq, pt, &plan);
-    if (plan_ws_bytes(p, plan.slots, rows) > ws_bytes || (plan.slots && !workspace)) {
+    slots = count_parts(p, n_seq, pt);
+    if (slots && (!workspace || plan_ws_bytes(p, slots, rows) > ws_bytes)) {
       pt = 0;  // the workspace cannot hold the split: run unsplit
-      make_plan(p, seq_ids, lens.data(), n_seq, 0, &plan);
+      slots = count_parts(p, n_seq, 0);
     }
   } else {
-    make_plan(p, seq_ids, lens.data(), n_seq, pt, &plan);
-    if (plan.slots && (!workspace || plan_ws_bytes(p, plan.slots, rows) > ws_bytes))
+    slots = count_parts(p, n_seq, pt);
+    if (slots && (!workspace || plan_ws_bytes(p, slots, rows) > ws_bytes))
       return set_err(PA_ERR_INVALID, "workspace too small for this partition size (see pa_workspace_size)");
   }
-  if (plan.slots * rows * static_cast<int64_t>(p->head_dim) > INT32_MAX * 4LL)
-    return set_err(PA_ERR_INVALID, "too many split partials");
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
 
-  std::vector<int32_t> w;
-  int n_tab = 0, n_len = 0;
-  size_t tab_off = 0, len_off = 0;
-  pack_dirty(p, w, &n_tab, &n_len, &tab_off, &len_off);
-  const size_t unit_off = pad8(w);
-  for (const pa::WorkUnit& u : plan.units) {
-    const int32_t* x = reinterpret_cast<const int32_t*>(&u);
-    w.insert(w.end(), x, x + 8);
+  // reuse the device plan when the batch and its partition structure are unchanged
+  std::vector<int32_t>& key = p->key_scratch;
+  key.assign({pt, n_seq});
+  for (int i = 0; i < n_seq; ++i) {
+    key.push_back(seq_ids[i]);
+    key.push_back(p->parts[i]);
   }
-  const size_t merge_off = pad8(w);
-  for (const pa::MergeUnit& m : plan.merges) {
-    const int32_t* x = reinterpret_cast<const int32_t*>(&m);
-    w.insert(w.end(), x, x + 4);
+  const bool replan = key != p->plan_key;
+  size_t plan_words = 0;
+  if (replan) {
+    make_plan(p, seq_ids, n_seq, pt);
+    plan_words = 8 * p->units.size() + 4 * p->merges.size();
+    int rc = ensure_dplan(p, plan_words * sizeof(int32_t));
+    if (rc != PA_OK) return rc;
   }
-  pad8(w);
-  int rc = upload(p, w, stream);
-  if (rc != PA_OK) return rc;
 
-  if (n_tab + n_len > 0) {
-    pa::AppendParams ap = base_append(p);
-    ap.tab = p->dmeta + tab_off;
-    ap.lens = p->dmeta + len_off;
-    ap.n_tab = n_tab;
-    ap.n_len = n_len;
+  p->bp.take_dirty(&p->dirty);
+  const size_t dw = dirty_words(p);
+  Stage* st = nullptr;
+  if (dw + plan_words > 0) {
+    int rc = acquire_stage(p, dw + plan_words, &st);
+    if (rc != PA_OK) return rc;
+  }
+  pa::AppendParams ap = base_append(p);
+  size_t off = 0;
+  if (st) write_dirty(p, st->host, st->dev, &off, &ap);
+  if (replan) {
+    int32_t* h = st->host + off;
+    std::memcpy(h, p->units.data(), 8 * p->units.size() * sizeof(int32_t));
+    std::memcpy(h + 8 * p->units.size(), p->merges.data(), 4 * p->merges.size() * sizeof(int32_t));
+    if (plan_words) {
+      hipError_t e = hipMemcpyAsync(p->dplan, h, plan_words * sizeof(int32_t), hipMemcpyHostToDevice, stream);
+      if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync(plan)");
+    }
+    p->plan_key.swap(key);
+    p->plan_units = static_cast<int>(p->units.size());
+    p->plan_merges = static_cast<int>(p->merges.size());
+  }
+  if (ap.n_tab + ap.n_len > 0) {
     hipError_t e = pa::launch_append(ap, stream);
     if (e != hipSuccess) return hip_err(e, "append kernel (table update)");
   }
-  if (plan.units.empty()) return PA_OK;
-
-  pa::AttnParams ak{};
-  ak.k_pool = p->k_pool;
-  ak.v_pool = p->v_pool;
-  ak.block_table = p->block_table;
-  ak.max_blocks = p->bp.max_blocks_per_seq();
-  ak.num_blocks = p->num_blocks;
-  ak.q = q;
-  ak.out = out;
-  ak.lse = lse;
-  float* ws = static_cast<float*>(workspace);
-  ak.ws_acc = ws;
-  ak.ws_ml = ws ? ws + static_cast<size_t>(plan.slots) * rows * p->head_dim : nullptr;
-  ak.units = reinterpret_cast<const pa::WorkUnit*>(p->dmeta + unit_off);
-  ak.merges = reinterpret_cast<const pa::MergeUnit*>(p->dmeta + merge_off);
-  ak.n_units = static_cast<int>(plan.units.size());
-  ak.n_merges = static_cast<int>(plan.merges.size());
-  ak.hkv = p->hkv;
-  ak.hq = num_q_heads;
-  ak.group = group;
-  ak.k_draft = k_draft;
-  ak.rows = rows;
-  ak.head_dim = p->head_dim;
-  ak.scale_log2 = scale * 1.4426950408889634f;
-  const pa::DType dt = static_cast<pa::DType>(p->dtype);
-  ProfEvent ev{};
-  prof_begin(p, 0, stream, &ev);
-  hipError_t e = pa::launch_attention(dt, ak, stream);
-  if (e != hipSuccess) return hip_err(e, "attention kernel");
-  prof_end(p, stream, &ev);
-  if (!plan.merges.empty()) {
-    ProfEvent ev2{};
-    prof_begin(p, 1, stream, &ev2);
-    e = pa::launch_merge(dt, ak, stream);
-    if (e != hipSuccess) return hip_err(e, "merge kernel");
-    prof_end(p, stream, &ev2);
+  if (p->plan_units > 0) {
+    pa::AttnParams ak{};
+    ak.k_pool = p->k_pool;
+    ak.v_pool = p->v_pool;
+    ak.block_table = p->block_table;
+    ak.seq_len = p->seq_len;
+    ak.max_blocks = p->bp.max_blocks_per_seq();
+    ak.num_blocks = p->num_blocks;
+    ak.part_tokens = pt;
+    ak.q = q;
+    ak.out = out;
+    ak.lse = lse;
+    float* ws = static_cast<float*>(workspace);
+    ak.ws_acc = ws;
+    ak.ws_ml = ws ? ws + static_cast<size_t>(slots) * rows * p->head_dim : nullptr;
+    ak.units = static_cast<const pa::WorkUnit*>(p->dplan);
+    ak.merges = reinterpret_cast<const pa::MergeUnit*>(static_cast<const int32_t*>(p->dplan) + 8 * p->plan_units);
+    ak.n_units = p->plan_units;
+    ak.n_merges = p->plan_merges;
+    ak.hkv = p->hkv;
+    ak.hq = num_q_heads;
+    ak.group = group;
+    ak.k_draft = k_draft;
+    ak.rows = rows;
+    ak.head_dim = p->head_dim;
+    ak.scale_log2 = scale * 1.4426950408889634f;
+    const pa::DType dt = static_cast<pa::DType>(p->dtype);
+    ProfEvent ev{};
+    prof_begin(p, 0, stream, &ev);
+    hipError_t e = pa::launch_attention(dt, ak, stream);
+    if (e != hipSuccess) return hip_err(e, "attention kernel");
+    prof_end(p, stream, &ev);
+    if (ak.n_merges > 0) {
+      ProfEvent ev2{};
+      prof_begin(p, 1, stream, &ev2);
+      e = pa::launch_merge(dt, ak, stream);
+      if (e != hipSuccess) return hip_err(e, "merge kernel");
+      prof_end(p, stream, &ev2);
+    }
   }
-  return PA_OK;
+  return st ? release_stage(st, stream) : PA_OK;
 }
 
 }  // namespace
@@ -394,9 +443,9 @@ int pa_destroy_pool(pa_pool* p) {
     hipEventDestroy(ev.start);
     hipEventDestroy(ev.stop);
   }
-  if (p->dmeta) {
+  if (p->dplan) {
     hipDeviceSynchronize();
-    hipFree(p->dmeta);
+    hipFree(p->dplan);
   }
   delete p;
   return PA_OK;
@@ -419,51 +468,40 @@ int pa_append_kv(pa_pool* p, const int32_t* seq_ids, int n_seq, const int32_t* n
   if (!p->host_only && total > 0 && (!aligned16(k_new) || !aligned16(v_new)))
     return set_err(PA_ERR_INVALID, "k_new and v_new must be 16-byte aligned");
   if (total > INT32_MAX / 2) return set_err(PA_ERR_INVALID, "too many rows in one append");
-  std::vector<int32_t> slots;
-  std::vector<pa::CowCopy> cows;
-  slots.reserve(static_cast<size_t>(total));
+  p->slots.clear();
+  p->cows.clear();
   std::string err;
-  int rc = p->bp.append(seq_ids, n_seq, n_tok, &slots, &cows, &err);
+  int rc = p->bp.append(seq_ids, n_seq, n_tok, &p->slots, &p->cows, &err);
   if (rc != pa::kOk) return set_err(rc, err);
-  if (p->host_only) {
-    pa::BlockPool::Dirty d;
-    p->bp.take_dirty(&d);
-    return PA_OK;
-  }
+  p->bp.take_dirty(&p->dirty);
+  if (p->host_only) return PA_OK;
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
-  std::vector<int32_t> w;
-  w.reserve(slots.size() + 64);
-  int n_tab = 0, n_len = 0;
-  size_t tab_off = 0, len_off = 0;
-  pack_dirty(p, w, &n_tab, &n_len, &tab_off, &len_off);
-  const size_t cow_off = pad8(w);
-  for (const pa::CowCopy& c : cows) {
-    w.push_back(c.src);
-    w.push_back(c.dst);
-    w.push_back(c.rows);
-  }
-  const size_t slot_off = pad8(w);
-  w.insert(w.end(), slots.begin(), slots.end());
-  pad8(w);
-  rc = upload(p, w, stream);
+  const size_t words = dirty_words(p) + pad8(3 * p->cows.size()) + pad8(p->slots.size());
+  Stage* st = nullptr;
+  rc = acquire_stage(p, words, &st);
   if (rc != PA_OK) return rc;
+  size_t off = 0;
   pa::AppendParams ap = base_append(p);
+  write_dirty(p, st->host, st->dev, &off, &ap);
+  ap.cows = st->dev + off;
+  for (const pa::CowCopy& c : p->cows) {
+    st->host[off++] = c.src;
+    st->host[off++] = c.dst;
+    st->host[off++] = c.rows;
+  }
+  off = pad8(off);
+  ap.slots = st->dev + off;
+  std::memcpy(st->host + off, p->slots.data(), p->slots.size() * sizeof(int32_t));
   ap.k_new = k_new;
   ap.v_new = v_new;
-  ap.tab = p->dmeta + tab_off;
-  ap.lens = p->dmeta + len_off;
-  ap.cows = p->dmeta + cow_off;
-  ap.slots = p->dmeta + slot_off;
-  ap.n_tab = n_tab;
-  ap.n_len = n_len;
-  ap.n_cow = static_cast<int>(cows.size());
-  ap.n_rows = static_cast<int>(slots.size());
+  ap.n_cow = static_cast<int>(p->cows.size());
+  ap.n_rows = static_cast<int>(p->slots.size());
   ProfEvent ev{};
   prof_begin(p, 2, stream, &ev);
   hipError_t e = pa::launch_append(ap, stream);
   if (e != hipSuccess) return hip_err(e, "append kernel");
   prof_end(p, stream, &ev);
-  return PA_OK;
+  return release_stage(st, stream);
 }
 
 int pa_decode(pa_pool* p, const int32_t* seq_ids, int n_seq, int num_q_heads, float scale,
@@ -490,13 +528,11 @@ int pa_truncate(pa_pool* p, int seq_id, int new_len) {
 int pa_truncate_batch(pa_pool* p, const int32_t* seq_ids, int n_seq, const int32_t* new_lens) {
   if (!p) return set_err(PA_ERR_INVALID, "pool is NULL");
   if (n_seq < 0 || (n_seq > 0 && (!seq_ids || !new_lens))) return set_err(PA_ERR_INVALID, "bad arrays");
-  std::vector<int32_t> seen;
-  seen.reserve(n_seq);
+  std::vector<int32_t> seen(seq_ids, seq_ids + n_seq);
   for (int i = 0; i < n_seq; ++i) {
     if (!p->bp.live(seq_ids[i])) return set_err(PA_ERR_INVALID, "sequence is not live");
     if (new_lens[i] < 0 || new_lens[i] > p->bp.length(seq_ids[i]))
       return set_err(PA_ERR_INVALID, "new_len outside [0, length]");
-    seen.push_back(seq_ids[i]);
   }
   std::sort(seen.begin(), seen.end());
   if (std::adjacent_find(seen.begin(), seen.end()) != seen.end())
@@ -515,27 +551,19 @@ int pa_free_seq(pa_pool* p, int seq_id) {
 
 int pa_sync_tables(pa_pool* p, void* stream_v) {
   if (!p) return set_err(PA_ERR_INVALID, "pool is NULL");
-  if (p->host_only) {
-    pa::BlockPool::Dirty d;
-    p->bp.take_dirty(&d);
-    return PA_OK;
-  }
   if (!p->bp.has_dirty()) return PA_OK;
+  p->bp.take_dirty(&p->dirty);
+  if (p->host_only) return PA_OK;
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
-  std::vector<int32_t> w;
-  int n_tab = 0, n_len = 0;
-  size_t tab_off = 0, len_off = 0;
-  pack_dirty(p, w, &n_tab, &n_len, &tab_off, &len_off);
-  pad8(w);
-  int rc = upload(p, w, stream);
+  Stage* st = nullptr;
+  int rc = acquire_stage(p, dirty_words(p), &st);
   if (rc != PA_OK) return rc;
+  size_t off = 0;
   pa::AppendParams ap = base_append(p);
-  ap.tab = p->dmeta + tab_off;
-  ap.lens = p->dmeta + len_off;
-  ap.n_tab = n_tab;
-  ap.n_len = n_len;
+  write_dirty(p, st->host, st->dev, &off, &ap);
   hipError_t e = pa::launch_append(ap, stream);
-  return e == hipSuccess ? PA_OK : hip_err(e, "append kernel (table update)");
+  if (e != hipSuccess) return hip_err(e, "append kernel (table update)");
+  return release_stage(st, stream);
 }
 
 int pa_workspace_size(const pa_pool* p, int n_seq, int num_q_heads, int k_draft, int max_tokens,

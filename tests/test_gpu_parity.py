@@ -311,3 +311,20 @@ def test_full_long():
 
 def test_full_verify():
     _full(make_verify(), [0, 33, 63])
+
+
+def test_many_partitions_fused_merge_and_repeat():
+    """129 partitions of 32 tokens for one sequence (more than one wave of
+    partials per merge), mixed with unsplit ones; a second identical call must
+    give bitwise the same result (the merge counters reset themselves)."""
+    w = make_custom(lengths=[4100, 70, 2000, 31], num_q_heads=16, num_kv_heads=4, head_dim=128, dtype="f16",
+                    seed=34)
+    pair = Pair(w)
+    pair.fill()
+    seqs = [0, 1, 2, 3]
+    out, lse = _decode(pair, seqs, w.q, w.scale, pt=32)
+    ro, rl = oracle_decode(pair, seqs, w.q, w.scale)
+    assert_close(out, lse, ro, rl, "f16", "129 partitions")
+    out2, lse2 = _decode(pair, seqs, w.q, w.scale, pt=32)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)) and torch.equal(lse, lse2)
