@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--separate", action="store_true",
+                    help="issue the append and the attention as two calls instead of pa_append_attend")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB before the timed region, so that "
@@ -93,7 +95,7 @@ def append_bytes(w) -> int:
 class Replica:
     """One filled pool plus the pre-marshalled arguments of a step."""
 
-    def __init__(self, w, pt):
+    def __init__(self, w, pt, separate=False):
         import torch
         from paged_kv_cache_216_amd.cache import PagedKVCache
 
@@ -135,16 +137,25 @@ class Replica:
         self.ws = c.make_workspace(b, w.num_q_heads, max_len, k_draft=w.k_draft, partition_tokens=pt)
         self.ws_bytes = 0 if self.ws is None else self.ws.numel() * 4
         self.pt = pt
+        self.separate = separate
 
     def step(self, stream_handle):
         from paged_kv_cache_216_amd import abi
         c, w, lib = self.cache, self.w, self.cache.lib
         h = c.handle
         vp = ctypes.c_void_p
+        ws = None if self.ws is None else vp(self.ws.data_ptr())
+        if self.t_new and not self.separate:
+            # append + attend in one call (one launch when possible)
+            abi.check(lib.pa_append_attend(h, self.ids, w.batch, self.t_new, vp(self.k_new.data_ptr()),
+                                           vp(self.v_new.data_ptr()), w.num_q_heads, w.scale,
+                                           vp(self.q.data_ptr()), vp(self.out.data_ptr()), vp(self.lse.data_ptr()),
+                                           self.pt, ws, self.ws_bytes, stream_handle))
+            abi.check(lib.pa_truncate_batch(h, self.ids, w.batch, self.rollback))
+            return
         if self.t_new:
             abi.check(lib.pa_append_kv(h, self.ids, w.batch, self.ntok, vp(self.k_new.data_ptr()),
                                        vp(self.v_new.data_ptr()), stream_handle))
-        ws = None if self.ws is None else vp(self.ws.data_ptr())
         if w.k_draft == 1:
             rc = lib.pa_decode(h, self.ids, w.batch, w.num_q_heads, w.scale, vp(self.q.data_ptr()),
                                vp(self.out.data_ptr()), vp(self.lse.data_ptr()), self.pt, ws, self.ws_bytes,
@@ -237,7 +248,7 @@ def main():
     w = make_workload(args.workload)
     pt = args.partition_tokens if args.partition_tokens else (w.partition_tokens or 0)
     print(f"bench: building {args.replicas} replica pools for '{w.name}'", file=sys.stderr, flush=True)
-    reps = [Replica(w, pt) for _ in range(args.replicas)]
+    reps = [Replica(w, pt, args.separate) for _ in range(args.replicas)]
     stream = torch.cuda.current_stream()
     sh = ctypes.c_void_p(stream.cuda_stream)
     if args.copy_calibration_mib:
@@ -303,6 +314,7 @@ def main():
                       "append": round(1e3 * kern[2][0] / max(1, kern[2][1]), 2) if kern[2][1] else None},
         "host_wall_ms_per_step": round(1e3 * wall / args.steps, 4),
         "host_enqueue_us_per_step": round(1e6 * t_enq / args.steps, 2),
+        "step_calls": "pa_append_kv + attention" if (args.separate or not reps[0].t_new) else "pa_append_attend",
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

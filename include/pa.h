@@ -147,6 +147,23 @@ int pa_verify(pa_pool* pool, const int32_t* seq_ids, int n_seq, int k_draft, int
               float scale, const void* q, void* out, float* lse, int partition_tokens,
               void* workspace, size_t ws_bytes, void* stream);
 
+/* pa_append_kv of n_new rows to each listed sequence followed by pa_verify
+ * with k_draft = n_new (n_new = 1: pa_decode), issued as one kernel launch
+ * when possible: the launch writes the rows into the pool while the attention
+ * takes the new rows straight from k_new / v_new.  Results are identical to
+ * the two separate calls.  Falls back to two launches (same results) when a
+ * write needs a copy-on-write copy first, when earlier table changes are still
+ * pending, or for PA_F32 pools.
+ *   seq_ids  host int32 [n_seq]; live and distinct
+ *   k_new, v_new  device [n_seq * n_new][num_kv_heads][head_dim], rows of
+ *            sequence i at i * n_new .. i * n_new + n_new - 1
+ *   q, out   device [n_seq][n_new][num_q_heads][head_dim]; lse [n_seq][n_new][num_q_heads] or NULL
+ * Other arguments and errors as pa_append_kv and pa_verify; nothing changes
+ * on error. */
+int pa_append_attend(pa_pool* pool, const int32_t* seq_ids, int n_seq, int n_new, const void* k_new,
+                     const void* v_new, int num_q_heads, float scale, const void* q, void* out, float* lse,
+                     int partition_tokens, void* workspace, size_t ws_bytes, void* stream);
+
 /* Cut sequence seq_id back to new_len tokens (0 <= new_len <= length), e.g. to
  * drop rejected drafts.  Blocks past ceil(new_len / 16) lose one reference and
  * go to the back of the free list, in logical order, when unreferenced. */

@@ -38,6 +38,7 @@ int BlockPool::init(int num_blocks, int max_seqs, int max_blocks_per_seq,
   seen_flag_.assign(max_seqs, 0);
   dirty_entry_list_.clear();
   dirty_len_list_.clear();
+  num_shared_ = 0;
   rc_delta_.assign(num_blocks, 0);
   touched_.clear();
   return kOk;
@@ -51,7 +52,9 @@ int32_t BlockPool::pop() {
 }
 
 void BlockPool::release(int32_t b) {
-  if (--rc_[b] == 0) free_.push_back(b);
+  const int32_t rc = --rc_[b];
+  if (rc == 1) --num_shared_;
+  if (rc == 0) free_.push_back(b);
 }
 
 int BlockPool::alloc(int seq, int parent, int shared_tokens, std::string* err) {
@@ -71,7 +74,7 @@ int BlockPool::alloc(int seq, int parent, int shared_tokens, std::string* err) {
   const std::vector<int32_t>& pt = tables_[parent];
   tables_[seq].assign(pt.begin(), pt.begin() + nb);
   for (int j = 0; j < nb; ++j) {
-    ++rc_[pt[j]];
+    if (++rc_[pt[j]] == 2) ++num_shared_;
     mark_entry(seq, j);
   }
   len_[seq] = shared_tokens;

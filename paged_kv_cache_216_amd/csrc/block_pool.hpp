@@ -50,6 +50,8 @@ class BlockPool {
   const std::vector<int32_t>& table(int seq) const { return tables_[seq]; }
   int refcount(int block) const { return rc_[block]; }
   int num_free() const { return static_cast<int>(free_.size()); }
+  // blocks referenced by more than one sequence
+  int num_shared() const { return num_shared_; }
   const std::deque<int32_t>& free_list() const { return free_; }
   int num_blocks() const { return num_blocks_; }
   int max_seqs() const { return max_seqs_; }
@@ -96,6 +98,7 @@ class BlockPool {
   std::vector<uint8_t> entry_flag_, len_flag_, seen_flag_;
   std::vector<int32_t> dirty_entry_list_, dirty_len_list_;
   std::vector<int32_t> rc_delta_, touched_;
+  int num_shared_ = 0;
 };
 
 }  // namespace pa

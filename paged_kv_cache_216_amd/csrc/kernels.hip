@@ -45,45 +45,49 @@ struct AppendGrid {
   int upd_blocks, cow_blocks, row_blocks;
 };
 
-__host__ __device__ inline AppendGrid append_grid(const AppendParams& p) {
+__host__ __device__ inline AppendGrid append_grid(const AppendParams& p, int nthreads) {
   AppendGrid g;
-  g.upd_blocks = (p.n_tab + p.n_len + kAppendThreads - 1) / kAppendThreads;
+  g.upd_blocks = (p.n_tab + p.n_len + nthreads - 1) / nthreads;
   g.cow_blocks = p.n_cow;
   const int chunks_per_row = p.hkv * p.head_dim * p.elem_bytes / 16;
   const long long work = static_cast<long long>(p.n_rows) * chunks_per_row;
-  g.row_blocks = static_cast<int>((work + kAppendThreads - 1) / kAppendThreads);
+  g.row_blocks = static_cast<int>((work + nthreads - 1) / nthreads);
   return g;
 }
 
+// Workgroup `b` (of nthreads threads) of the append work.  Table and length
+// updates, copies of the filled slots of shared blocks (rows [0, off) only, so
+// they never overlap the slots this call writes), and one 16-byte chunk of a
+// new row per thread.
 template <int E>  // element bytes: 2 or 4
-__global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) {
+__device__ inline void append_work(const AppendParams& p, const int32_t* meta, int b, int nthreads) {
   using Elem = std::conditional_t<E == 2, uint16_t, uint32_t>;
   constexpr int X = 16 / E;  // elements per 16-byte chunk
-  const AppendGrid g = append_grid(p);
+  const AppendGrid g = append_grid(p, nthreads);
   const int D = p.head_dim;
   const int nchunk = D / X;                               // chunks per (head, slot)
   const size_t page = static_cast<size_t>(D) * kBlk;      // elements per (block, head)
-  int b = blockIdx.x;
+  const int tid = threadIdx.x;
 
   if (b < g.upd_blocks) {
-    const int i = b * kAppendThreads + threadIdx.x;
+    const int i = b * nthreads + tid;
     if (i < p.n_tab) {
-      p.block_table[p.tab[2 * i]] = p.tab[2 * i + 1];
+      p.block_table[meta[p.tab + 2 * i]] = meta[p.tab + 2 * i + 1];
     } else if (i < p.n_tab + p.n_len) {
       const int k = i - p.n_tab;
-      p.seq_len[p.lens[2 * k]] = p.lens[2 * k + 1];
+      p.seq_len[meta[p.lens + 2 * k]] = meta[p.lens + 2 * k + 1];
     }
     return;
   }
   b -= g.upd_blocks;
 
   if (b < g.cow_blocks) {
-    const int src = p.cows[3 * b], dst = p.cows[3 * b + 1], rows = p.cows[3 * b + 2];
+    const int src = meta[p.cows + 3 * b], dst = meta[p.cows + 3 * b + 1], rows = meta[p.cows + 3 * b + 2];
     // K: 16-byte chunks (head, chunk, slot < rows)
     const u32x4* ks = reinterpret_cast<const u32x4*>(p.k_pool) + static_cast<size_t>(src) * p.hkv * nchunk * kBlk;
     u32x4* kd = reinterpret_cast<u32x4*>(p.k_pool) + static_cast<size_t>(dst) * p.hkv * nchunk * kBlk;
     const int kwork = p.hkv * nchunk * rows;
-    for (int w = threadIdx.x; w < kwork; w += kAppendThreads) {
+    for (int w = tid; w < kwork; w += nthreads) {
       const int t = w % rows;
       const int hc = w / rows;  // head * nchunk + chunk
       kd[hc * kBlk + t] = ks[hc * kBlk + t];
@@ -92,7 +96,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) 
     const Elem* vs = reinterpret_cast<const Elem*>(p.v_pool) + static_cast<size_t>(src) * p.hkv * page;
     Elem* vd = reinterpret_cast<Elem*>(p.v_pool) + static_cast<size_t>(dst) * p.hkv * page;
     const int vwork = p.hkv * D * rows;
-    for (int w = threadIdx.x; w < vwork; w += kAppendThreads) {
+    for (int w = tid; w < vwork; w += nthreads) {
       const int t = w % rows;
       const int hd = w / rows;  // head * D + dim
       vd[hd * kBlk + t] = vs[hd * kBlk + t];
@@ -103,13 +107,13 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) 
 
   // rows: one thread per 16-byte chunk of one row (all heads)
   const int chunks_per_row = p.hkv * nchunk;
-  const long long w = static_cast<long long>(b) * kAppendThreads + threadIdx.x;
+  const long long w = static_cast<long long>(b) * nthreads + tid;
   if (w >= static_cast<long long>(p.n_rows) * chunks_per_row) return;
   const int row = static_cast<int>(w / chunks_per_row);
   const int c = static_cast<int>(w % chunks_per_row);  // head * nchunk + chunk
   const int h = c / nchunk;
   const int cc = c % nchunk;
-  const int slot = p.slots[row];
+  const int slot = meta[p.slots + row];
   const int phys = slot / kBlk;
   const int t = slot % kBlk;
   const u32x4 kv = reinterpret_cast<const u32x4*>(p.k_new)[static_cast<size_t>(row) * chunks_per_row + c];
@@ -121,6 +125,11 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) 
                static_cast<size_t>(cc) * X * kBlk + t;
 #pragma unroll
   for (int i = 0; i < X; ++i) vdst[i * kBlk] = vsrc[i];
+}
+
+template <int E>
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p, InlineMeta im) {
+  append_work<E>(p, p.ext ? p.ext : im.w, blockIdx.x, kAppendThreads);
 }
 
 // ----------------------------------------------------------------------------
@@ -185,12 +194,27 @@ __device__ inline float shfl_f(float x, int src_lane) {
 
 __device__ inline int readlane(int x, int lane) { return __builtin_amdgcn_readlane(x, lane); }
 
-// K/V pages are read once per launch: load them with the non-temporal hint so
-// they stream past the caches instead of evicting the tables and queries.
-template <typename V>
-__device__ inline V stream_load(const V* p) {
-  return __builtin_nontemporal_load(p);
+// Buffer resource over one K or V page: loads at byte offsets >= `bytes`
+// return zero without a memory access (word 3 is the gfx9 raw-buffer format).
+__device__ inline __amdgpu_buffer_rsrc_t page_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
+
+// cache policy bit 1 = non-temporal
+template <bool NTL>
+__device__ inline u32x4 page_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, NTL ? 2 : 0));
+}
+
+template <bool NTL>
+__device__ inline u32x2 page_load8(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, NTL ? 2 : 0));
+}
+
+// Without shared blocks every K/V page is read once per launch, so it is
+// loaded with the non-temporal hint and streams past the caches instead of
+// evicting the tables and queries.  Shared (copy-on-write) blocks are read by
+// several sequences and are better kept in cache.
 
 // zero the 16-bit elements of an 8-byte V fragment whose token position >= n
 __device__ inline u32x2 mask_v16(u32x2 v, int pos0, int n) {
@@ -222,11 +246,12 @@ struct Unit {
 };
 
 // 16-bit element types: bf16 or f16
-template <typename T, int D, int NT>
+template <typename T, int D, int NT, bool NTL, bool FUSED>
 __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) {
   using Op = typename MfmaOp<T>::type;
   constexpr int KS = D / 32;  // QK k-steps per block
   constexpr int DC = D / 16;  // output dim chunks
+  constexpr int kPageBytes = D * kBlk * static_cast<int>(sizeof(T));
   const int lane = threadIdx.x;
   const int col = lane & 15;
   const int grp = lane >> 4;
@@ -269,8 +294,16 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
   const size_t page = static_cast<size_t>(D) * kBlk;
   const int32_t* bt = p.block_table + static_cast<size_t>(u.seq) * p.max_blocks;
   const int jb0 = u.tok_begin / kBlk;
-  const int nblk = (u.tok_end + kBlk - 1) / kBlk - jb0;
   const int mask_from = u.n - p.k_draft;  // positions above this may be masked for some row
+  // Rows appended by this very launch (fused append) are not read from the
+  // pool, which other workgroups of the launch are writing: the pool pass stops
+  // at the last pair boundary before them, and a tail step processes the
+  // remaining pairs with the new rows taken from k_new / v_new -- the same
+  // pairs, hence the same arithmetic, as when the append was a separate launch.
+  const int pool_end = FUSED
+      ? min(u.tok_end, u.tok_begin + max(0, (u.n - p.t_new - u.tok_begin) / (2 * kBlk)) * (2 * kBlk))
+      : u.tok_end;
+  const int nblk = pool_end > u.tok_begin ? (pool_end + kBlk - 1) / kBlk - jb0 : 0;
 
   // One pair of blocks = one PV step.  The loads of pair j+1 are issued before
   // pair j is computed, so each wave keeps 16-32 KiB of K/V in flight (except
@@ -279,6 +312,75 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
     Op k0[KS], k1[KS];
     u32x2 v0[DC], v1[DC];
   };
+  // Scores, online softmax and PV for the 32 tokens starting at pos0; tokens at
+  // or beyond `end` are masked (and their V zeroed: such slots may hold anything).
+  auto process = [&](Frag& f, int pos0, int end) {
+    const bool need_mask = (pos0 + 2 * kBlk - 1 > mask_from) || (pos0 + 2 * kBlk > end);
+    Op pa[NT];
+    float a4[NT][4];
+    // scores and online-softmax update for every row tile (needs K only)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        s0 = MfmaOp<T>::mma(f.k0[s], qop[nt][s], s0);
+        s1 = MfmaOp<T>::mma(f.k1[s], qop[nt][s], s1);
+      }
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = s0[e] * p.scale_log2;
+        x[4 + e] = s1[e] * p.scale_log2;
+      }
+      if (need_mask) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int pos = pos0 + (e >> 2) * kBlk + 4 * grp + (e & 3);
+          const bool ok = pos < end && pos <= lim[nt];
+          x[e] = ok ? x[e] : kNegInf;
+        }
+      }
+      float mt = x[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
+      mt = wave_max_groups(mt);
+      const float m_new = fmaxf(m_run[nt], mt);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(x[e] - m_use);
+        ps += pe;
+        pa[nt][e] = static_cast<T>(pe);
+      }
+      l_run[nt] = l_run[nt] * alpha + ps;
+      m_run[nt] = m_new;
+      // rescale factors move to the accumulator layout: lane holds rows 4*grp + jj
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) a4[nt][jj] = shfl_f(alpha, 4 * grp + jj);
+    }
+    if (pos0 + 2 * kBlk > end) {
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        f.v0[c] = mask_v16(f.v0[c], pos0 + 4 * grp, end);
+        f.v1[c] = mask_v16(f.v1[c], pos0 + kBlk + 4 * grp, end);
+      }
+    }
+    // O = diag(alpha) O + P V
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[nt][c][jj] *= a4[nt][jj];
+        const Op vb = __builtin_bit_cast(Op, u32x4{f.v0[c][0], f.v0[c][1], f.v1[c][0], f.v1[c][1]});
+        acc[nt][c] = MfmaOp<T>::mma(pa[nt], vb, acc[nt][c]);
+      }
+    }
+  };
+
   for (int cb = 0; cb < nblk; cb += 64) {
     const int cnt = min(64, nblk - cb);
     const int tb = (lane < cnt) ? bt[jb0 + cb + lane] : 0;  // this chunk of the table, one entry per lane
@@ -286,114 +388,119 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
     // a table entry outside the pool can only come from a host-side bug; clamp
     // it so that the bug shows as a wrong result, never as a stray access
     auto phys_at = [&](int j) { return min(max(readlane(tb, j), 0), p.num_blocks - 1); };
-    // Branch-free: a pair past the end (or the missing second block of an odd
-    // count) re-reads blocks already requested, which hit in cache, and every
-    // position it contributes is masked.  Uniform control flow lets the
-    // compiler wait only for the pair being computed.
+    // Branch-free loads through bounded buffer resources: a pair past the end
+    // of the unit, or the missing second block of an odd count, gets a
+    // resource with no valid bytes, so its loads return zeros and touch no
+    // memory.  Uniform control flow lets the compiler wait only for the pair
+    // being computed.
     auto load = [&](Frag& f, int pj) {
-      const int j = min(2 * pj, cnt - 1);
-      const int phys0 = phys_at(j);
+      const int j = 2 * pj;
+      const int bytes0 = j < cnt ? kPageBytes : 0;
+      const int bytes1 = j + 1 < cnt ? kPageBytes : 0;
+      const int phys0 = phys_at(min(j, cnt - 1));
       const int phys1 = phys_at(min(j + 1, cnt - 1));
-      const T* kp0 = kpool + (static_cast<size_t>(phys0) * p.hkv + kvh) * page;
-      const T* vp0 = vpool + (static_cast<size_t>(phys0) * p.hkv + kvh) * page;
-      const T* kp1 = kpool + (static_cast<size_t>(phys1) * p.hkv + kvh) * page;
-      const T* vp1 = vpool + (static_cast<size_t>(phys1) * p.hkv + kvh) * page;
+      const size_t off0 = (static_cast<size_t>(phys0) * p.hkv + kvh) * page;
+      const size_t off1 = (static_cast<size_t>(phys1) * p.hkv + kvh) * page;
+      const auto rk0 = page_rsrc(kpool + off0, bytes0), rv0 = page_rsrc(vpool + off0, bytes0);
+      const auto rk1 = page_rsrc(kpool + off1, bytes1), rv1 = page_rsrc(vpool + off1, bytes1);
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        f.k0[s] = __builtin_bit_cast(Op, stream_load(reinterpret_cast<const u32x4*>(kp0 + ((4 * s + grp) * kBlk + col) * 8)));
+        f.k0[s] = __builtin_bit_cast(Op, page_load16<NTL>(rk0, ((4 * s + grp) * kBlk + col) * 16));
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        f.k1[s] = __builtin_bit_cast(Op, stream_load(reinterpret_cast<const u32x4*>(kp1 + ((4 * s + grp) * kBlk + col) * 8)));
+        f.k1[s] = __builtin_bit_cast(Op, page_load16<NTL>(rk1, ((4 * s + grp) * kBlk + col) * 16));
 #pragma unroll
-      for (int c = 0; c < DC; ++c) f.v0[c] = stream_load(reinterpret_cast<const u32x2*>(vp0 + (16 * c + col) * kBlk + 4 * grp));
+      for (int c = 0; c < DC; ++c) f.v0[c] = page_load8<NTL>(rv0, ((16 * c + col) * kBlk + 4 * grp) * 2);
 #pragma unroll
-      for (int c = 0; c < DC; ++c) f.v1[c] = stream_load(reinterpret_cast<const u32x2*>(vp1 + (16 * c + col) * kBlk + 4 * grp));
+      for (int c = 0; c < DC; ++c) f.v1[c] = page_load8<NTL>(rv1, ((16 * c + col) * kBlk + 4 * grp) * 2);
     };
-    auto process = [&](Frag& f, int pj) {
-      const int pos0 = (jb0 + cb + 2 * pj) * kBlk;  // first token of the pair
-      const bool need_mask = (pos0 + 2 * kBlk - 1 > mask_from) || (pos0 + 2 * kBlk > u.tok_end);
-      Op pa[NT];
-      float a4[NT][4];
-      // scores and online-softmax update for every row tile (needs K only)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          s0 = MfmaOp<T>::mma(f.k0[s], qop[nt][s], s0);
-          s1 = MfmaOp<T>::mma(f.k1[s], qop[nt][s], s1);
-        }
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[e] = s0[e] * p.scale_log2;
-          x[4 + e] = s1[e] * p.scale_log2;
-        }
-        if (need_mask) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int pos = pos0 + (e >> 2) * kBlk + 4 * grp + (e & 3);
-            const bool ok = pos < u.tok_end && pos <= lim[nt];
-            x[e] = ok ? x[e] : kNegInf;
-          }
-        }
-        float mt = x[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
-        mt = wave_max_groups(mt);
-        const float m_new = fmaxf(m_run[nt], mt);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
-        float ps = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pe = __builtin_amdgcn_exp2f(x[e] - m_use);
-          ps += pe;
-          pa[nt][e] = static_cast<T>(pe);
-        }
-        l_run[nt] = l_run[nt] * alpha + ps;
-        m_run[nt] = m_new;
-        // rescale factors move to the accumulator layout: lane holds rows 4*grp + jj
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) a4[nt][jj] = shfl_f(alpha, 4 * grp + jj);
-      }
-      // slots past the end of the sequence may hold anything: zero their V
-      if (pos0 + 2 * kBlk > u.n) {
-#pragma unroll
-        for (int c = 0; c < DC; ++c) {
-          f.v0[c] = mask_v16(f.v0[c], pos0 + 4 * grp, u.n);
-          f.v1[c] = mask_v16(f.v1[c], pos0 + kBlk + 4 * grp, u.n);
-        }
-      }
-      // O = diag(alpha) O + P V
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-        for (int c = 0; c < DC; ++c) {
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) acc[nt][c][jj] *= a4[nt][jj];
-          const Op vb = __builtin_bit_cast(Op, u32x4{f.v0[c][0], f.v0[c][1], f.v1[c][0], f.v1[c][1]});
-          acc[nt][c] = MfmaOp<T>::mma(pa[nt], vb, acc[nt][c]);
-        }
-      }
-    };
+    const int base_pos = (jb0 + cb) * kBlk;
     if constexpr (D * NT < 512) {
       Frag fa, fb;
       load(fa, 0);
       for (int pj = 0; pj < npairs; pj += 2) {
-        load(fb, min(pj + 1, npairs - 1));
-        process(fa, pj);
+        load(fb, pj + 1);
+        process(fa, base_pos + 2 * pj * kBlk, pool_end);
         if (pj + 1 >= npairs) break;
-        load(fa, min(pj + 2, npairs - 1));
-        process(fb, pj + 1);
+        load(fa, pj + 2);
+        process(fb, base_pos + (2 * pj + 2) * kBlk, pool_end);
       }
     } else {
       // the largest query tiles leave no registers for a second pair in flight
       for (int pj = 0; pj < npairs; ++pj) {
         Frag fa;
         load(fa, pj);
-        process(fa, pj);
+        process(fa, base_pos + 2 * pj * kBlk, pool_end);
       }
+    }
+  }
+
+  // Tail step of a fused append: the pairs from pool_end to the end of the
+  // partition.  Old rows come from the pool (blocks holding no old row are
+  // not read), the rows this launch appends ([n - t_new, n)) from
+  // k_new / v_new ([n_seq * t_new][hkv][D], rows of query row q at q * t_new ..).
+  if constexpr (FUSED) {
+    const int old_end = u.n - p.t_new;
+    const size_t rstride = static_cast<size_t>(p.hkv) * D;  // elements between new rows
+    const T* kn = static_cast<const T*>(p.app.k_new) + (static_cast<size_t>(u.q_row) * p.t_new * p.hkv + kvh) * D;
+    const uint16_t* vn =
+        static_cast<const uint16_t*>(p.app.v_new) + (static_cast<size_t>(u.q_row) * p.t_new * p.hkv + kvh) * D;
+#pragma unroll 1
+    for (int pos0 = pool_end; pos0 < u.tok_end; pos0 += 2 * kBlk) {
+      Frag f;
+      const int blk0 = pos0 / kBlk;
+      const bool old0 = blk0 * kBlk < old_end;
+      const bool old1 = (blk0 + 1) * kBlk < old_end;
+      const int phys0 = old0 ? min(max(bt[blk0], 0), p.num_blocks - 1) : 0;
+      const int phys1 = old1 ? min(max(bt[blk0 + 1], 0), p.num_blocks - 1) : 0;
+      const size_t off0 = (static_cast<size_t>(phys0) * p.hkv + kvh) * page;
+      const size_t off1 = (static_cast<size_t>(phys1) * p.hkv + kvh) * page;
+      const auto rk0 = page_rsrc(kpool + off0, old0 ? kPageBytes : 0), rv0 = page_rsrc(vpool + off0, old0 ? kPageBytes : 0);
+      const auto rk1 = page_rsrc(kpool + off1, old1 ? kPageBytes : 0), rv1 = page_rsrc(vpool + off1, old1 ? kPageBytes : 0);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        f.k0[s] = __builtin_bit_cast(Op, page_load16<false>(rk0, ((4 * s + grp) * kBlk + col) * 16));
+        f.k1[s] = __builtin_bit_cast(Op, page_load16<false>(rk1, ((4 * s + grp) * kBlk + col) * 16));
+      }
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        f.v0[c] = page_load8<false>(rv0, ((16 * c + col) * kBlk + 4 * grp) * 2);
+        f.v1[c] = page_load8<false>(rv1, ((16 * c + col) * kBlk + 4 * grp) * 2);
+      }
+      // splice in the new rows, one token at a time (selects, no divergent branches)
+      const int i_end = min(pos0 + 2 * kBlk, u.n);
+#pragma unroll 1
+      for (int i = max(pos0, old_end); i < i_end; ++i) {
+        const int rel = i - pos0;
+        const int b = rel >> 4;
+        const int t = rel & 15;
+        const size_t row = static_cast<size_t>(i - old_end) * rstride;
+        const bool kl = col == t;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const Op x = __builtin_bit_cast(Op, *reinterpret_cast<const u32x4*>(kn + row + 32 * s + 8 * grp));
+          if (b == 0)
+            f.k0[s] = kl ? x : f.k0[s];
+          else
+            f.k1[s] = kl ? x : f.k1[s];
+        }
+        const bool vl = grp == (t >> 2);
+        const int word = (t & 3) >> 1;
+        const int shift = (t & 1) * 16;
+        const uint32_t keep = ~(0xFFFFu << shift);
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          const uint32_t bits = static_cast<uint32_t>(vn[row + 16 * c + col]) << shift;
+          if (b == 0) {
+            const uint32_t w = (f.v0[c][word] & keep) | bits;
+            f.v0[c][word] = vl ? w : f.v0[c][word];
+          } else {
+            const uint32_t w = (f.v1[c][word] & keep) | bits;
+            f.v1[c][word] = vl ? w : f.v1[c][word];
+          }
+        }
+      }
+      process(f, pos0, u.tok_end);
     }
   }
 
@@ -598,8 +705,9 @@ __device__ inline void attn_body32(const AttnParams& p, const Unit& u, int kvh) 
   }
 }
 
-template <typename T, int D, int NT>
-__global__ __launch_bounds__(64) void attn_kernel(AttnParams p) {
+// One workgroup (one wave) per (work unit, key/value head).
+template <typename T, int D, int NT, bool NTL, bool FUSED>
+__device__ inline void attn_unit(const AttnParams& p, const int32_t* meta) {
   const int unit = blockIdx.x / p.hkv;
   const int kvh = blockIdx.x - unit * p.hkv;
   const WorkUnit w = p.units[unit];
@@ -609,14 +717,38 @@ __global__ __launch_bounds__(64) void attn_kernel(AttnParams p) {
   u.slot_base = w.slot_base;
   u.nparts = w.nparts;
   u.part = w.part;
-  // the length mirror is bounded by the table row the host allocated
-  u.n = min(p.seq_len[w.seq], p.max_blocks * kBlk);
+  // the length is bounded by the table row the host allocated
+  // (readfirstlane: the value is wave-uniform, and saying so keeps the page
+  // addresses derived from it in scalar registers)
+  const int n = FUSED ? __builtin_amdgcn_readfirstlane(meta[p.lens_by_row + w.q_row]) : p.seq_len[w.seq];
+  u.n = min(n, p.max_blocks * kBlk);
   u.tok_begin = w.nparts > 1 ? w.part * p.part_tokens : 0;
   u.tok_end = w.nparts > 1 ? min(u.n, u.tok_begin + p.part_tokens) : u.n;
   if constexpr (std::is_same_v<T, float>)
     attn_body32<D, NT>(p, u, kvh);
   else
-    attn_body16<T, D, NT>(p, u, kvh);
+    attn_body16<T, D, NT, NTL, FUSED>(p, u, kvh);
+}
+
+template <typename T, int D, int NT, bool NTL>
+__global__ __launch_bounds__(64) void attn_kernel(AttnParams p) {
+  attn_unit<T, D, NT, NTL, false>(p, nullptr);
+}
+
+// Attention and append in one launch: workgroups past the attention grid do
+// the append work (table / length updates and the scatter of the new rows).
+// (two waves per SIMD for the single-tile 128-dim case: the pool pass needs
+// them to keep enough loads in flight)
+template <typename T, int D, int NT, bool NTL>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 && D == 128 ? 2 : 1)))
+void attn_append_kernel(AttnParams p, InlineMeta im) {
+  const int32_t* meta = p.app.ext ? p.app.ext : im.w;
+  const int n_attn = p.n_units * p.hkv;
+  if (static_cast<int>(blockIdx.x) >= n_attn) {
+    append_work<static_cast<int>(sizeof(T))>(p.app, meta, blockIdx.x - n_attn, 64);
+    return;
+  }
+  attn_unit<T, D, NT, NTL, true>(p, meta);
 }
 
 // Exact merge of one output row of a split sequence, one 256-thread workgroup
@@ -693,27 +825,41 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
   }
 }
 
-template <typename T, int D>
-hipError_t launch_attn_d(const AttnParams& p, hipStream_t stream) {
+template <typename T, int D, int NT, bool NTL>
+void launch_attn_nt(const AttnParams& p, const InlineMeta& m, hipStream_t stream) {
+  if constexpr (!std::is_same_v<T, float>) {
+    if (p.t_new > 0) {
+      const dim3 grid(static_cast<unsigned>(p.n_units) * p.hkv + p.app_blocks);
+      hipLaunchKernelGGL((attn_append_kernel<T, D, NT, NTL>), grid, dim3(64), 0, stream, p, m);
+      return;
+    }
+  }
   const dim3 grid(static_cast<unsigned>(p.n_units) * p.hkv);
+  hipLaunchKernelGGL((attn_kernel<T, D, NT, NTL>), grid, dim3(64), 0, stream, p);
+}
+
+template <typename T, int D, bool NTL>
+hipError_t launch_attn_d(const AttnParams& p, const InlineMeta& m, hipStream_t stream) {
+  if (std::is_same_v<T, float> && p.t_new > 0) return hipErrorInvalidValue;  // no fused fp32 path
   const int nt = (p.rows + 15) / 16;
   if (nt <= 1)
-    hipLaunchKernelGGL((attn_kernel<T, D, 1>), grid, dim3(64), 0, stream, p);
+    launch_attn_nt<T, D, 1, NTL>(p, m, stream);
   else if (nt <= 2)
-    hipLaunchKernelGGL((attn_kernel<T, D, 2>), grid, dim3(64), 0, stream, p);
+    launch_attn_nt<T, D, 2, NTL>(p, m, stream);
   else if constexpr (D <= 128)
-    hipLaunchKernelGGL((attn_kernel<T, D, 4>), grid, dim3(64), 0, stream, p);
+    launch_attn_nt<T, D, 4, NTL>(p, m, stream);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_attn_t(const AttnParams& p, hipStream_t stream) {
+hipError_t launch_attn_t(const AttnParams& p, const InlineMeta& m, hipStream_t stream) {
+  const bool ntl = p.stream_kv != 0 && !std::is_same_v<T, float>;
   switch (p.head_dim) {
-    case 64: return launch_attn_d<T, 64>(p, stream);
-    case 128: return launch_attn_d<T, 128>(p, stream);
-    case 256: return launch_attn_d<T, 256>(p, stream);
+    case 64: return ntl ? launch_attn_d<T, 64, true>(p, m, stream) : launch_attn_d<T, 64, false>(p, m, stream);
+    case 128: return ntl ? launch_attn_d<T, 128, true>(p, m, stream) : launch_attn_d<T, 128, false>(p, m, stream);
+    case 256: return ntl ? launch_attn_d<T, 256, true>(p, m, stream) : launch_attn_d<T, 256, false>(p, m, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -722,15 +868,22 @@ hipError_t launch_attn_t(const AttnParams& p, hipStream_t stream) {
 
 int max_rows_for_head_dim(int head_dim) { return head_dim <= 128 ? 64 : 32; }
 
-hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
-  const AppendGrid g = append_grid(p);
+int append_blocks64(const AppendParams& p) {
+  const AppendGrid g = append_grid(p, 64);
+  return g.upd_blocks + g.cow_blocks + g.row_blocks;
+}
+
+hipError_t launch_append(const AppendParams& p, const InlineMeta* meta, hipStream_t stream) {
+  const AppendGrid g = append_grid(p, kAppendThreads);
   const long long blocks = static_cast<long long>(g.upd_blocks) + g.cow_blocks + g.row_blocks;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (p.elem_bytes == 2)
-    hipLaunchKernelGGL((append_kernel<2>), dim3(static_cast<unsigned>(blocks)), dim3(kAppendThreads), 0, stream, p);
+    hipLaunchKernelGGL((append_kernel<2>), dim3(static_cast<unsigned>(blocks)), dim3(kAppendThreads), 0, stream, p,
+                       *meta);
   else
-    hipLaunchKernelGGL((append_kernel<4>), dim3(static_cast<unsigned>(blocks)), dim3(kAppendThreads), 0, stream, p);
+    hipLaunchKernelGGL((append_kernel<4>), dim3(static_cast<unsigned>(blocks)), dim3(kAppendThreads), 0, stream, p,
+                       *meta);
   return hipGetLastError();
 }
 
@@ -757,12 +910,12 @@ hipError_t launch_merge(DType dt, const AttnParams& p, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_attention(DType dt, const AttnParams& p, hipStream_t stream) {
-  if (p.n_units == 0) return hipSuccess;
+hipError_t launch_attention(DType dt, const AttnParams& p, const InlineMeta* meta, hipStream_t stream) {
+  if (p.n_units == 0 && (p.t_new == 0 || p.app_blocks == 0)) return hipSuccess;
   switch (dt) {
-    case kBF16: return launch_attn_t<__bf16>(p, stream);
-    case kF16: return launch_attn_t<_Float16>(p, stream);
-    case kF32: return launch_attn_t<float>(p, stream);
+    case kBF16: return launch_attn_t<__bf16>(p, *meta, stream);
+    case kF16: return launch_attn_t<_Float16>(p, *meta, stream);
+    case kF32: return launch_attn_t<float>(p, *meta, stream);
   }
   return hipErrorInvalidValue;
 }

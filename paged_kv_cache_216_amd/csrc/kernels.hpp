@@ -10,9 +10,16 @@ namespace pa {
 
 enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
-// One launch applies pending device-table updates, copy-on-write block copies
-// and the scatter of new rows.  The int32 metadata is read by the kernel
-// straight from pinned host memory:
+// Per-call int32 metadata travels inside the launch's kernel arguments when it
+// fits (no copy, no host-memory reads from the GPU); larger metadata is read by
+// the kernel from pinned host memory (`ext` below).
+constexpr int kInlineWords = 2048;
+struct InlineMeta {
+  int32_t w[kInlineWords];
+};
+
+// Table updates, copy-on-write block copies and the scatter of new rows.
+// Offsets are in int32 words into the call's metadata:
 //   tab  [n_tab][2]  (flat table index, physical block)
 //   lens [n_len][2]  (sequence, length)
 //   cows [n_cow][3]  (src block, dst block, rows to copy)
@@ -24,18 +31,17 @@ struct AppendParams {
   int32_t* seq_len;
   const void* k_new;
   const void* v_new;
-  const int32_t* tab;
-  const int32_t* lens;
-  const int32_t* cows;
-  const int32_t* slots;
+  const int32_t* ext;  // metadata in pinned host memory, or nullptr: inline
+  int tab, lens, cows, slots;
   int n_tab, n_len, n_cow, n_rows;
   int hkv, head_dim, elem_bytes;
 };
 
 // Work unit of the attention kernel, one per (sequence, partition); the
 // key/value head comes from the grid.  Lengths are not part of the unit: the
-// kernel reads them from the device length mirror, so a plan stays valid while
-// sequences grow inside their partitions.
+// kernel reads them from the device length mirror (or, when the launch also
+// appends, from the call's metadata), so a plan stays valid while sequences
+// grow inside their partitions.
 struct WorkUnit {
   int32_t q_row;      // index of the sequence in q / out (0..n_seq-1)
   int32_t seq;        // row of the block table and of the length mirror
@@ -73,11 +79,23 @@ struct AttnParams {
   int hkv, hq, group, k_draft, rows;  // rows = group * k_draft
   int head_dim;
   float scale_log2;   // scale * log2(e)
+  int stream_kv;      // 1: no block is shared, read K/V pages with the non-temporal hint
+  // Fused append (t_new > 0): this launch also appends t_new rows per sequence.
+  // Attention reads the new rows from k_new / v_new ([n_seq * t_new][hkv][D],
+  // row q_row * t_new + i) and the lengths after the append from the metadata
+  // at `lens_by_row`; `app` (run by `app_blocks` extra workgroups) writes the
+  // rows into the pool and updates the table and length mirrors.
+  int t_new;
+  int lens_by_row;
+  int app_blocks;
+  AppendParams app;
 };
 
-hipError_t launch_append(const AppendParams& p, hipStream_t stream);
-hipError_t launch_attention(DType dt, const AttnParams& p, hipStream_t stream);
+hipError_t launch_append(const AppendParams& p, const InlineMeta* meta, hipStream_t stream);
+hipError_t launch_attention(DType dt, const AttnParams& p, const InlineMeta* meta, hipStream_t stream);
 hipError_t launch_merge(DType dt, const AttnParams& p, hipStream_t stream);
+// Workgroups of 64 threads that the append work of `p` needs.
+int append_blocks64(const AppendParams& p);
 // Largest supported rows (group * k_draft) for a head dim.
 int max_rows_for_head_dim(int head_dim);
 

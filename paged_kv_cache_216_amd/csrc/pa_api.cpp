@@ -1,14 +1,15 @@
 // C-ABI entry points declared in include/pa.h.
 //
-// Host side of every device call: validate, update the block allocator, write
-// the call's per-call metadata (table updates, copies, slots) into one pinned,
-// device-visible host buffer, and launch the kernels, which read that buffer
-// directly -- no separate host-to-device copy is enqueued.  A ring of such
-// buffers, each released by an event recorded after the last kernel that reads
-// it, lets the host run ahead of the GPU.  The attention work plan (which
-// sequence / partition each workgroup takes) lives in device memory and is
-// re-uploaded only when the batch or its partition structure changes; lengths
-// come from the device length mirror.
+// Host side of every device call: validate, update the block allocator,
+// assemble the call's metadata (table updates, copies, slots, lengths) and
+// launch the kernels.  Metadata up to 8 KiB travels inside the launch's kernel
+// arguments; larger metadata (bulk appends) is written to a pinned,
+// device-visible host buffer that the kernel reads directly, from a ring whose
+// buffers are released by events recorded after their last reader.  The
+// attention work plan (which sequence / partition each workgroup takes) lives
+// in device memory and is re-uploaded only when the batch or its partition
+// structure changes; lengths come from the device length mirror, or from the
+// metadata when the launch itself appends.
 #include "../../include/pa.h"
 
 #include <hip/hip_runtime.h>
@@ -53,8 +54,6 @@ struct ProfEvent {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-size_t pad8(size_t n) { return (n + 7) & ~size_t(7); }
-
 }  // namespace
 
 struct pa_pool {
@@ -81,6 +80,10 @@ struct pa_pool {
   std::vector<pa::WorkUnit> units, tail_units;
   std::vector<pa::MergeUnit> merges;
   std::vector<int> lens, parts;
+  std::vector<int32_t> ntok;
+  // call metadata being assembled, and its kernel-argument copy
+  std::vector<int32_t> meta;
+  pa::InlineMeta inline_meta;
   // profiling
   bool prof = false;
   std::vector<ProfEvent> prof_events;
@@ -163,29 +166,45 @@ pa::AppendParams base_append(pa_pool* p) {
   return ap;
 }
 
-// Write the pending table / length updates at host[*off]; fills ap.
-void write_dirty(pa_pool* p, int32_t* host, int32_t* dev, size_t* off, pa::AppendParams* ap) {
-  const pa::BlockPool::Dirty& d = p->dirty;
-  size_t o = *off;
-  ap->tab = dev + o;
-  for (size_t i = 0; i < d.table_idx.size(); ++i) {
-    host[o++] = d.table_idx[i];
-    host[o++] = d.table_val[i];
-  }
-  o = pad8(o);
-  ap->lens = dev + o;
-  for (size_t i = 0; i < d.len_seq.size(); ++i) {
-    host[o++] = d.len_seq[i];
-    host[o++] = d.len_val[i];
-  }
-  o = pad8(o);
-  ap->n_tab = static_cast<int>(d.table_idx.size());
-  ap->n_len = static_cast<int>(d.len_seq.size());
-  *off = o;
+size_t pad8(std::vector<int32_t>& w) {
+  while (w.size() % 8) w.push_back(0);
+  return w.size();
 }
 
-size_t dirty_words(const pa_pool* p) {
-  return pad8(2 * p->dirty.table_idx.size()) + pad8(2 * p->dirty.len_seq.size());
+// Append the pending table / length updates to the call's metadata.
+void meta_dirty(pa_pool* p, pa::AppendParams* ap) {
+  const pa::BlockPool::Dirty& d = p->dirty;
+  std::vector<int32_t>& w = p->meta;
+  ap->tab = static_cast<int>(pad8(w));
+  for (size_t i = 0; i < d.table_idx.size(); ++i) {
+    w.push_back(d.table_idx[i]);
+    w.push_back(d.table_val[i]);
+  }
+  ap->lens = static_cast<int>(pad8(w));
+  for (size_t i = 0; i < d.len_seq.size(); ++i) {
+    w.push_back(d.len_seq[i]);
+    w.push_back(d.len_val[i]);
+  }
+  ap->n_tab = static_cast<int>(d.table_idx.size());
+  ap->n_len = static_cast<int>(d.len_seq.size());
+}
+
+// Make the assembled metadata visible to the next launches: inline (kernel
+// arguments) when it fits, else a pinned ring buffer (*st set; release it
+// after the last launch that reads it).
+int meta_submit(pa_pool* p, const int32_t** ext, Stage** st) {
+  *st = nullptr;
+  *ext = nullptr;
+  const size_t n = p->meta.size();
+  if (n <= static_cast<size_t>(pa::kInlineWords)) {
+    std::memcpy(p->inline_meta.w, p->meta.data(), n * sizeof(int32_t));
+    return PA_OK;
+  }
+  int rc = acquire_stage(p, n, st);
+  if (rc != PA_OK) return rc;
+  std::memcpy((*st)->host, p->meta.data(), n * sizeof(int32_t));
+  *ext = (*st)->dev;
+  return PA_OK;
 }
 
 int rows_limit(const pa_pool* p) { return pa::max_rows_for_head_dim(p->head_dim); }
@@ -240,9 +259,62 @@ size_t plan_ws_bytes(const pa_pool* p, int64_t slots, int rows) {
   return static_cast<size_t>(slots) * rows * (p->head_dim + 2) * sizeof(float);
 }
 
+// Launch an update-only append kernel for the pending table / length changes.
+int flush_dirty(pa_pool* p, hipStream_t stream) {
+  if (!p->bp.has_dirty()) return PA_OK;
+  p->bp.take_dirty(&p->dirty);
+  if (p->host_only) return PA_OK;
+  p->meta.clear();
+  pa::AppendParams ap = base_append(p);
+  meta_dirty(p, &ap);
+  Stage* st = nullptr;
+  int rc = meta_submit(p, &ap.ext, &st);
+  if (rc != PA_OK) return rc;
+  hipError_t e = pa::launch_append(ap, &p->inline_meta, stream);
+  if (e != hipSuccess) return hip_err(e, "append kernel (table update)");
+  return st ? release_stage(st, stream) : PA_OK;
+}
+
+// Host bookkeeping for an append is done and its dirty set taken; enqueue its
+// kernel (table / length updates, copies, row scatter).
+int launch_append_call(pa_pool* p, const void* k_new, const void* v_new, hipStream_t stream) {
+  p->meta.clear();
+  pa::AppendParams ap = base_append(p);
+  meta_dirty(p, &ap);
+  ap.cows = static_cast<int>(pad8(p->meta));
+  for (const pa::CowCopy& c : p->cows) {
+    p->meta.push_back(c.src);
+    p->meta.push_back(c.dst);
+    p->meta.push_back(c.rows);
+  }
+  ap.slots = static_cast<int>(pad8(p->meta));
+  p->meta.insert(p->meta.end(), p->slots.begin(), p->slots.end());
+  ap.k_new = k_new;
+  ap.v_new = v_new;
+  ap.n_cow = static_cast<int>(p->cows.size());
+  ap.n_rows = static_cast<int>(p->slots.size());
+  Stage* st = nullptr;
+  int rc = meta_submit(p, &ap.ext, &st);
+  if (rc != PA_OK) return rc;
+  ProfEvent ev{};
+  prof_begin(p, 2, stream, &ev);
+  hipError_t e = pa::launch_append(ap, &p->inline_meta, stream);
+  if (e != hipSuccess) return hip_err(e, "append kernel");
+  prof_end(p, stream, &ev);
+  return st ? release_stage(st, stream) : PA_OK;
+}
+
+struct AppendSpec {
+  int t_new;
+  const void* k_new;
+  const void* v_new;
+};
+
+// Attention over the current lengths; with `app`, first append app->t_new rows
+// to every sequence, in the same launch when possible.
 int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q_heads, float scale,
            const void* q, void* out, float* lse, int partition_tokens, void* workspace, size_t ws_bytes,
-           void* stream_v) {
+           void* stream_v, const AppendSpec* app) {
   if (!p) return set_err(PA_ERR_INVALID, "pool is NULL");
   if (p->host_only) return set_err(PA_ERR_STATE, "host-only pool has no device memory");
   if (n_seq < 0) return set_err(PA_ERR_INVALID, "n_seq < 0");
@@ -259,11 +331,16 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   if (n_seq > 0 && (!seq_ids || !q || !out)) return set_err(PA_ERR_INVALID, "seq_ids, q or out is NULL");
   if (!aligned16(q) || !aligned16(out) || !aligned16(workspace))
     return set_err(PA_ERR_INVALID, "q, out and workspace must be 16-byte aligned");
+  const int t_new = app ? app->t_new : 0;
+  if (app && (t_new < 1 || (n_seq > 0 && (!app->k_new || !app->v_new))))
+    return set_err(PA_ERR_INVALID, "n_new must be >= 1 and k_new / v_new given");
+  if (app && (!aligned16(app->k_new) || !aligned16(app->v_new)))
+    return set_err(PA_ERR_INVALID, "k_new and v_new must be 16-byte aligned");
   p->lens.resize(n_seq);
   for (int i = 0; i < n_seq; ++i) {
     const int s = seq_ids[i];
     if (!p->bp.live(s)) return set_err(PA_ERR_INVALID, "attention over a sequence that is not live");
-    p->lens[i] = p->bp.length(s);
+    p->lens[i] = p->bp.length(s) + t_new;  // length when the attention runs
     if (p->lens[i] < std::max(1, k_draft))
       return set_err(PA_ERR_INVALID, "sequence shorter than max(1, k_draft)");
   }
@@ -283,6 +360,33 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   }
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
 
+  // The append: host bookkeeping first (all-or-nothing; the last check that can fail).
+  bool fused = false;
+  if (app) {
+    p->ntok.assign(n_seq, t_new);
+    const bool table_pending = p->bp.dirty_entries() > 0;
+    p->slots.clear();
+    p->cows.clear();
+    std::string err;
+    int rc = p->bp.append(seq_ids, n_seq, p->ntok.data(), &p->slots, &p->cows, &err);
+    if (rc != pa::kOk) return set_err(rc, err);
+    // One launch can append and attend when no copy-on-write copy has to land
+    // first and no earlier table change is still on its way to the device: the
+    // attention reads the table while the launch's append work writes it, which
+    // is safe only for the blocks this append opens (their only valid rows are
+    // the new ones, which the attention takes from k_new / v_new).
+    fused = p->cows.empty() && !table_pending && p->dtype != PA_F32;
+    if (!fused) {
+      p->bp.take_dirty(&p->dirty);
+      rc = launch_append_call(p, app->k_new, app->v_new, stream);
+      if (rc != PA_OK) return rc;
+    }
+  }
+  if (!fused) {
+    int rc = flush_dirty(p, stream);
+    if (rc != PA_OK) return rc;
+  }
+
   // reuse the device plan when the batch and its partition structure are unchanged
   std::vector<int32_t>& key = p->key_scratch;
   key.assign({pt, n_seq});
@@ -290,80 +394,87 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
     key.push_back(seq_ids[i]);
     key.push_back(p->parts[i]);
   }
-  const bool replan = key != p->plan_key;
-  size_t plan_words = 0;
-  if (replan) {
+  if (key != p->plan_key) {
     make_plan(p, seq_ids, n_seq, pt);
-    plan_words = 8 * p->units.size() + 4 * p->merges.size();
+    const size_t plan_words = 8 * p->units.size() + 4 * p->merges.size();
     int rc = ensure_dplan(p, plan_words * sizeof(int32_t));
     if (rc != PA_OK) return rc;
-  }
-
-  p->bp.take_dirty(&p->dirty);
-  const size_t dw = dirty_words(p);
-  Stage* st = nullptr;
-  if (dw + plan_words > 0) {
-    int rc = acquire_stage(p, dw + plan_words, &st);
-    if (rc != PA_OK) return rc;
-  }
-  pa::AppendParams ap = base_append(p);
-  size_t off = 0;
-  if (st) write_dirty(p, st->host, st->dev, &off, &ap);
-  if (replan) {
-    int32_t* h = st->host + off;
-    std::memcpy(h, p->units.data(), 8 * p->units.size() * sizeof(int32_t));
-    std::memcpy(h + 8 * p->units.size(), p->merges.data(), 4 * p->merges.size() * sizeof(int32_t));
     if (plan_words) {
-      hipError_t e = hipMemcpyAsync(p->dplan, h, plan_words * sizeof(int32_t), hipMemcpyHostToDevice, stream);
+      Stage* pst = nullptr;
+      rc = acquire_stage(p, plan_words, &pst);
+      if (rc != PA_OK) return rc;
+      std::memcpy(pst->host, p->units.data(), 8 * p->units.size() * sizeof(int32_t));
+      std::memcpy(pst->host + 8 * p->units.size(), p->merges.data(), 4 * p->merges.size() * sizeof(int32_t));
+      hipError_t e = hipMemcpyAsync(p->dplan, pst->host, plan_words * sizeof(int32_t), hipMemcpyHostToDevice, stream);
       if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync(plan)");
+      rc = release_stage(pst, stream);
+      if (rc != PA_OK) return rc;
     }
     p->plan_key.swap(key);
     p->plan_units = static_cast<int>(p->units.size());
     p->plan_merges = static_cast<int>(p->merges.size());
   }
-  if (ap.n_tab + ap.n_len > 0) {
-    hipError_t e = pa::launch_append(ap, stream);
-    if (e != hipSuccess) return hip_err(e, "append kernel (table update)");
+
+  pa::AttnParams ak{};
+  ak.k_pool = p->k_pool;
+  ak.v_pool = p->v_pool;
+  ak.block_table = p->block_table;
+  ak.seq_len = p->seq_len;
+  ak.max_blocks = p->bp.max_blocks_per_seq();
+  ak.num_blocks = p->num_blocks;
+  ak.part_tokens = pt;
+  ak.q = q;
+  ak.out = out;
+  ak.lse = lse;
+  float* ws = static_cast<float*>(workspace);
+  ak.ws_acc = ws;
+  ak.ws_ml = ws ? ws + static_cast<size_t>(slots) * rows * p->head_dim : nullptr;
+  ak.units = static_cast<const pa::WorkUnit*>(p->dplan);
+  ak.merges = reinterpret_cast<const pa::MergeUnit*>(static_cast<const int32_t*>(p->dplan) + 8 * p->plan_units);
+  ak.n_units = p->plan_units;
+  ak.n_merges = p->plan_merges;
+  ak.hkv = p->hkv;
+  ak.hq = num_q_heads;
+  ak.group = group;
+  ak.k_draft = k_draft;
+  ak.rows = rows;
+  ak.head_dim = p->head_dim;
+  ak.scale_log2 = scale * 1.4426950408889634f;
+  ak.stream_kv = p->bp.num_shared() == 0 ? 1 : 0;
+  ak.app = base_append(p);
+  Stage* st = nullptr;
+  if (fused) {
+    // metadata: this append's table / length updates, the new rows' slots, and
+    // the length of every query row after the append
+    p->bp.take_dirty(&p->dirty);
+    p->meta.clear();
+    meta_dirty(p, &ak.app);
+    ak.app.slots = static_cast<int>(pad8(p->meta));
+    p->meta.insert(p->meta.end(), p->slots.begin(), p->slots.end());
+    ak.lens_by_row = static_cast<int>(pad8(p->meta));
+    p->meta.insert(p->meta.end(), p->lens.begin(), p->lens.end());
+    ak.app.k_new = app->k_new;
+    ak.app.v_new = app->v_new;
+    ak.app.n_rows = static_cast<int>(p->slots.size());
+    ak.t_new = t_new;
+    ak.app_blocks = pa::append_blocks64(ak.app);
+    int rc = meta_submit(p, &ak.app.ext, &st);
+    if (rc != PA_OK) return rc;
   }
-  if (p->plan_units > 0) {
-    pa::AttnParams ak{};
-    ak.k_pool = p->k_pool;
-    ak.v_pool = p->v_pool;
-    ak.block_table = p->block_table;
-    ak.seq_len = p->seq_len;
-    ak.max_blocks = p->bp.max_blocks_per_seq();
-    ak.num_blocks = p->num_blocks;
-    ak.part_tokens = pt;
-    ak.q = q;
-    ak.out = out;
-    ak.lse = lse;
-    float* ws = static_cast<float*>(workspace);
-    ak.ws_acc = ws;
-    ak.ws_ml = ws ? ws + static_cast<size_t>(slots) * rows * p->head_dim : nullptr;
-    ak.units = static_cast<const pa::WorkUnit*>(p->dplan);
-    ak.merges = reinterpret_cast<const pa::MergeUnit*>(static_cast<const int32_t*>(p->dplan) + 8 * p->plan_units);
-    ak.n_units = p->plan_units;
-    ak.n_merges = p->plan_merges;
-    ak.hkv = p->hkv;
-    ak.hq = num_q_heads;
-    ak.group = group;
-    ak.k_draft = k_draft;
-    ak.rows = rows;
-    ak.head_dim = p->head_dim;
-    ak.scale_log2 = scale * 1.4426950408889634f;
-    const pa::DType dt = static_cast<pa::DType>(p->dtype);
+  const pa::DType dt = static_cast<pa::DType>(p->dtype);
+  if (ak.n_units > 0 || fused) {
     ProfEvent ev{};
     prof_begin(p, 0, stream, &ev);
-    hipError_t e = pa::launch_attention(dt, ak, stream);
+    hipError_t e = pa::launch_attention(dt, ak, &p->inline_meta, stream);
     if (e != hipSuccess) return hip_err(e, "attention kernel");
     prof_end(p, stream, &ev);
-    if (ak.n_merges > 0) {
-      ProfEvent ev2{};
-      prof_begin(p, 1, stream, &ev2);
-      e = pa::launch_merge(dt, ak, stream);
-      if (e != hipSuccess) return hip_err(e, "merge kernel");
-      prof_end(p, stream, &ev2);
-    }
+  }
+  if (ak.n_merges > 0) {
+    ProfEvent ev{};
+    prof_begin(p, 1, stream, &ev);
+    hipError_t e = pa::launch_merge(dt, ak, stream);
+    if (e != hipSuccess) return hip_err(e, "merge kernel");
+    prof_end(p, stream, &ev);
   }
   return st ? release_stage(st, stream) : PA_OK;
 }
@@ -475,47 +586,29 @@ int pa_append_kv(pa_pool* p, const int32_t* seq_ids, int n_seq, const int32_t* n
   if (rc != pa::kOk) return set_err(rc, err);
   p->bp.take_dirty(&p->dirty);
   if (p->host_only) return PA_OK;
-  hipStream_t stream = static_cast<hipStream_t>(stream_v);
-  const size_t words = dirty_words(p) + pad8(3 * p->cows.size()) + pad8(p->slots.size());
-  Stage* st = nullptr;
-  rc = acquire_stage(p, words, &st);
-  if (rc != PA_OK) return rc;
-  size_t off = 0;
-  pa::AppendParams ap = base_append(p);
-  write_dirty(p, st->host, st->dev, &off, &ap);
-  ap.cows = st->dev + off;
-  for (const pa::CowCopy& c : p->cows) {
-    st->host[off++] = c.src;
-    st->host[off++] = c.dst;
-    st->host[off++] = c.rows;
-  }
-  off = pad8(off);
-  ap.slots = st->dev + off;
-  std::memcpy(st->host + off, p->slots.data(), p->slots.size() * sizeof(int32_t));
-  ap.k_new = k_new;
-  ap.v_new = v_new;
-  ap.n_cow = static_cast<int>(p->cows.size());
-  ap.n_rows = static_cast<int>(p->slots.size());
-  ProfEvent ev{};
-  prof_begin(p, 2, stream, &ev);
-  hipError_t e = pa::launch_append(ap, stream);
-  if (e != hipSuccess) return hip_err(e, "append kernel");
-  prof_end(p, stream, &ev);
-  return release_stage(st, stream);
+  return launch_append_call(p, k_new, v_new, static_cast<hipStream_t>(stream_v));
 }
 
 int pa_decode(pa_pool* p, const int32_t* seq_ids, int n_seq, int num_q_heads, float scale,
               const void* q, void* out, float* lse, int partition_tokens, void* workspace,
               size_t ws_bytes, void* stream) {
   return attend(p, seq_ids, n_seq, 1, num_q_heads, scale, q, out, lse, partition_tokens, workspace,
-                ws_bytes, stream);
+                ws_bytes, stream, nullptr);
 }
 
 int pa_verify(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q_heads, float scale,
               const void* q, void* out, float* lse, int partition_tokens, void* workspace,
               size_t ws_bytes, void* stream) {
   return attend(p, seq_ids, n_seq, k_draft, num_q_heads, scale, q, out, lse, partition_tokens, workspace,
-                ws_bytes, stream);
+                ws_bytes, stream, nullptr);
+}
+
+int pa_append_attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int n_new, const void* k_new,
+                     const void* v_new, int num_q_heads, float scale, const void* q, void* out, float* lse,
+                     int partition_tokens, void* workspace, size_t ws_bytes, void* stream) {
+  const AppendSpec app{n_new, k_new, v_new};
+  return attend(p, seq_ids, n_seq, n_new, num_q_heads, scale, q, out, lse, partition_tokens, workspace,
+                ws_bytes, stream, &app);
 }
 
 int pa_truncate(pa_pool* p, int seq_id, int new_len) {
@@ -551,19 +644,7 @@ int pa_free_seq(pa_pool* p, int seq_id) {
 
 int pa_sync_tables(pa_pool* p, void* stream_v) {
   if (!p) return set_err(PA_ERR_INVALID, "pool is NULL");
-  if (!p->bp.has_dirty()) return PA_OK;
-  p->bp.take_dirty(&p->dirty);
-  if (p->host_only) return PA_OK;
-  hipStream_t stream = static_cast<hipStream_t>(stream_v);
-  Stage* st = nullptr;
-  int rc = acquire_stage(p, dirty_words(p), &st);
-  if (rc != PA_OK) return rc;
-  size_t off = 0;
-  pa::AppendParams ap = base_append(p);
-  write_dirty(p, st->host, st->dev, &off, &ap);
-  hipError_t e = pa::launch_append(ap, stream);
-  if (e != hipSuccess) return hip_err(e, "append kernel (table update)");
-  return release_stage(st, stream);
+  return flush_dirty(p, static_cast<hipStream_t>(stream_v));
 }
 
 int pa_workspace_size(const pa_pool* p, int n_seq, int num_q_heads, int k_draft, int max_tokens,

@@ -328,3 +328,82 @@ def test_many_partitions_fused_merge_and_repeat():
     out2, lse2 = _decode(pair, seqs, w.q, w.scale, pt=32)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16)) and torch.equal(lse, lse2)
+
+
+def _fused_vs_separate(w, prefix_fork_partial=False, pending_fork=False):
+    """Run the same step as append + attend (two calls) and as one
+    pa_append_attend call: pools, tables and outputs must be bitwise equal."""
+    pairs = []
+    for fused in (False, True):
+        pair = Pair(w, max_seqs=2 * w.batch + 2)
+        pair.fill()
+        if pending_fork:
+            # a child sharing only full blocks of sequence 1: its table entries
+            # are still pending, and no write needs a copy
+            full = (int(pair.model.length(1)) // 16) * 16
+            pair.alloc(w.batch, 1, full)
+        seqs = list(range(w.batch))
+        t = w.new_k.shape[1]
+        nk = to_torch(w.new_k.reshape(-1, w.num_kv_heads, w.head_dim), w.dtype)
+        nv = to_torch(w.new_v.reshape(-1, w.num_kv_heads, w.head_dim), w.dtype)
+        q = to_torch(w.q, w.dtype)
+        ws = pair.gpu.make_workspace(w.batch, w.num_q_heads, int(w.final_lengths().max()), k_draft=t)
+        if fused:
+            out, lse = pair.gpu.append_attend(seqs, nk, nv, q.contiguous(), w.scale, workspace=ws)
+        else:
+            pair.gpu.append(seqs, [t] * w.batch, nk, nv)
+            if t == 1:
+                out, lse = pair.gpu.decode(seqs, q[:, 0].contiguous(), w.scale, workspace=ws)
+                out, lse = out[:, None], lse[:, None]
+            else:
+                out, lse = pair.gpu.verify(seqs, q.contiguous(), w.scale, workspace=ws)
+        pair.model.append(seqs, [t] * w.batch, w.new_k.reshape(-1, w.num_kv_heads, w.head_dim),
+                          w.new_v.reshape(-1, w.num_kv_heads, w.head_dim))
+        torch.cuda.synchronize()
+        pair.check_pools_and_tables()
+        pairs.append((pair, out.clone(), lse.clone()))
+    it = torch.int32 if w.dtype == "f32" else torch.int16
+    (_, o1, l1), (p2, o2, l2) = pairs
+    assert torch.equal(o1.view(it), o2.view(it)), "fused and separate outputs differ"
+    assert torch.equal(l1, l2)
+    return p2, o2, l2
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_append_attend_decode_matches_separate_and_oracle(dtype):
+    w = make_custom(lengths=[15, 16, 31, 200, 513, 1000, 1, 47], mode="append_decode", num_q_heads=32,
+                    num_kv_heads=8, head_dim=128, dtype=dtype, seed=40)
+    pair, out, lse = _fused_vs_separate(w)
+    seqs = list(range(w.batch))
+    ro, rl = oracle_decode(pair, seqs, w.q, w.scale)
+    assert_close(out, lse, ro, rl, dtype, "fused decode step")
+
+
+def test_append_attend_verify_shared_prefix():
+    w = make_custom(lengths=[16, 77, 5, 300], mode="verify", num_q_heads=32, num_kv_heads=8, head_dim=128,
+                    dtype="bf16", seed=41, k_draft=5, prefix_len=256)
+    pair, out, lse = _fused_vs_separate(w)
+    ro, rl = oracle_decode(pair, list(range(w.batch)), w.q, w.scale, k_draft=5)
+    assert_close(out, lse, ro, rl, "bf16", "fused verify")
+
+
+def test_append_attend_copy_on_write_falls_back():
+    # a 250-token shared prefix leaves a shared partial block: the first write
+    # into it needs a copy, so the library issues separate launches
+    w = make_custom(lengths=[0, 0, 0], mode="verify", num_q_heads=16, num_kv_heads=4, head_dim=64,
+                    dtype="f16", seed=42, k_draft=3, prefix_len=250)
+    _fused_vs_separate(w)
+
+
+def test_append_attend_with_pending_table_falls_back():
+    w = make_custom(lengths=[40, 90], mode="append_decode", num_q_heads=8, num_kv_heads=2, head_dim=128,
+                    dtype="bf16", seed=43)
+    _fused_vs_separate(w, pending_fork=True)
+
+
+def test_append_attend_fp32():
+    w = make_custom(lengths=[17, 64], mode="append_decode", num_q_heads=4, num_kv_heads=4, head_dim=64,
+                    dtype="f32", seed=44, scale=0.125)
+    pair, out, lse = _fused_vs_separate(w)
+    ro, rl = oracle_decode(pair, [0, 1], w.q, w.scale)
+    assert_close(out, lse, ro, rl, "f32", "fp32 append+attend")
