@@ -240,10 +240,25 @@ __device__ inline void store_elem(T* p, float v) {
   *p = static_cast<T>(v);
 }
 
-// A work unit with its token range resolved against the current length.
+// A work unit.  `n_raw` is the sequence length as read (mirror or launch
+// metadata); the bodies resolve the token range from it after their first
+// loads are issued, so that those loads do not wait for the length.
 struct Unit {
-  int q_row, seq, n, tok_begin, tok_end, slot_base, nparts, part;
+  int q_row, seq, n_raw, tok_begin, slot_base, nparts, part;
 };
+
+struct Range {
+  int n, tok_end;
+};
+
+// (readfirstlane: the length is wave-uniform, and saying so keeps the page
+// addresses derived from it in scalar registers)
+__device__ inline Range resolve(const AttnParams& p, const Unit& u, int n_raw) {
+  Range r;
+  r.n = min(__builtin_amdgcn_readfirstlane(n_raw), p.max_blocks * kBlk);  // bounded by the table row
+  r.tok_end = u.nparts > 1 ? min(r.n, u.tok_begin + p.part_tokens) : r.n;
+  return r;
+}
 
 // 16-bit element types: bf16 or f16
 template <typename T, int D, int NT, bool NTL, bool FUSED>
@@ -258,25 +273,42 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
   const int rows = p.rows;
   const int G = p.group;
 
-  // ---- queries (B operand of S^T = K Q^T), per row tile
+  const T* kpool = static_cast<const T*>(p.k_pool);
+  const T* vpool = static_cast<const T*>(p.v_pool);
+  const size_t page = static_cast<size_t>(D) * kBlk;
+  const int32_t* bt = p.block_table + static_cast<size_t>(u.seq) * p.max_blocks;
+  const int jb0 = u.tok_begin / kBlk;
+
+  // ---- first loads, none of which needs the length: the queries (B operand
+  // of S^T = K Q^T) and the first 64 entries of the unit's table row (entries
+  // past the row read as zero, entries past the unit are never used).  Tile
+  // rows past `rows` repeat the last query row: their softmax is computed and
+  // dropped, and it does not touch the other rows.
   Op qop[NT][KS];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int rr = min(nt * 16 + col, rows - 1);
+    const int i = rr / G, g = rr - i * G;
+    const T* qp = static_cast<const T*>(p.q) + (static_cast<size_t>(u.q_row * p.k_draft + i) * p.hq + kvh * G + g) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qop[nt][s] = __builtin_bit_cast(Op, *reinterpret_cast<const u32x4*>(qp + 32 * s + 8 * grp));
+  }
+  const auto trow = page_rsrc(bt, p.max_blocks * 4);
+  int tb_next = __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(trow, (jb0 + lane) * 4, 0, 0));
+  // The wait for the length goes here, below the loads above: the empty asm
+  // statement is the first use of the loaded value, and the compiler moves no
+  // memory access across it.
+  int n_raw = u.n_raw;
+  asm volatile("" : "+v"(n_raw));
+  const Range rg = resolve(p, u, n_raw);
+  const int n = rg.n;
+  const int tok_end = rg.tok_end;
   int lim[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = nt * 16 + col;
-    if (r < rows) {
-      const int i = r / G, g = r - (r / G) * G;
-      const T* qp = static_cast<const T*>(p.q) +
-                    (static_cast<size_t>(u.q_row * p.k_draft + i) * p.hq + kvh * G + g) * D;
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        qop[nt][s] = __builtin_bit_cast(Op, *reinterpret_cast<const u32x4*>(qp + 32 * s + 8 * grp));
-      lim[nt] = u.n - p.k_draft + i;
-    } else {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) qop[nt][s] = Op{};
-      lim[nt] = u.n - 1;
-    }
+    lim[nt] = n - p.k_draft + min(r, rows - 1) / G;
   }
 
   f32x4 acc[NT][DC];
@@ -289,25 +321,18 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
     for (int c = 0; c < DC; ++c) acc[nt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const T* kpool = static_cast<const T*>(p.k_pool);
-  const T* vpool = static_cast<const T*>(p.v_pool);
-  const size_t page = static_cast<size_t>(D) * kBlk;
-  const int32_t* bt = p.block_table + static_cast<size_t>(u.seq) * p.max_blocks;
-  const int jb0 = u.tok_begin / kBlk;
-  const int mask_from = u.n - p.k_draft;  // positions above this may be masked for some row
+  const int mask_from = n - p.k_draft;  // positions above this may be masked for some row
   // Rows appended by this very launch (fused append) are not read from the
   // pool, which other workgroups of the launch are writing: the pool pass stops
   // at the last pair boundary before them, and a tail step processes the
   // remaining pairs with the new rows taken from k_new / v_new -- the same
   // pairs, hence the same arithmetic, as when the append was a separate launch.
   const int pool_end = FUSED
-      ? min(u.tok_end, u.tok_begin + max(0, (u.n - p.t_new - u.tok_begin) / (2 * kBlk)) * (2 * kBlk))
-      : u.tok_end;
+      ? min(tok_end, u.tok_begin + max(0, (n - p.t_new - u.tok_begin) / (2 * kBlk)) * (2 * kBlk))
+      : tok_end;
   const int nblk = pool_end > u.tok_begin ? (pool_end + kBlk - 1) / kBlk - jb0 : 0;
 
-  // One pair of blocks = one PV step.  The loads of pair j+1 are issued before
-  // pair j is computed, so each wave keeps 16-32 KiB of K/V in flight (except
-  // for the largest query tiles, whose accumulators need those registers).
+  // One pair of blocks = one PV step (K and V of 32 tokens, 16 KiB at D = 128).
   struct Frag {
     Op k0[KS], k1[KS];
     u32x2 v0[DC], v1[DC];
@@ -381,13 +406,20 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
     }
   };
 
-  for (int cb = 0; cb < nblk; cb += 64) {
-    const int cnt = min(64, nblk - cb);
-    const int tb = (lane < cnt) ? bt[jb0 + cb + lane] : 0;  // this chunk of the table, one entry per lane
+  // The table row, 64 entries per chunk, one per lane; each chunk's successor
+  // is requested while the chunk is processed.
+  // (a do-while: the first chunk is entered whatever the length, so that
+  // nothing in it waits on the length before its table entries are requested;
+  // with no block in range every load below reads zero and touches no memory)
+  int cb = 0;
+  do {
+    const int cnt = max(0, min(64, nblk - cb));
+    const int tb = tb_next;
+    tb_next = __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(trow, (jb0 + cb + 64 + lane) * 4, 0, 0));
     const int npairs = (cnt + 1) >> 1;
     // a table entry outside the pool can only come from a host-side bug; clamp
     // it so that the bug shows as a wrong result, never as a stray access
-    auto phys_at = [&](int j) { return min(max(readlane(tb, j), 0), p.num_blocks - 1); };
+    auto phys_at = [&](int j) { return min(max(readlane(tb, j & 63), 0), p.num_blocks - 1); };
     // Branch-free loads through bounded buffer resources: a pair past the end
     // of the unit, or the missing second block of an odd count, gets a
     // resource with no valid bytes, so its loads return zeros and touch no
@@ -415,7 +447,12 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       for (int c = 0; c < DC; ++c) f.v1[c] = page_load8<NTL>(rv1, ((16 * c + col) * kBlk + 4 * grp) * 2);
     };
     const int base_pos = (jb0 + cb) * kBlk;
-    if constexpr (D * NT < 512) {
+    // One pair in flight per wave is enough to saturate HBM with two waves
+    // per SIMD, and fewer bytes queued in the memory system shorten every
+    // dependent access (measured on MI355X: 3-6 % faster than keeping two
+    // pairs in flight).  Multi-tile (verify) waves do more math per pair and
+    // keep the second pair in flight.
+    if constexpr (NT >= 2 && D * NT < 512) {
       Frag fa, fb;
       load(fa, 0);
       for (int pj = 0; pj < npairs; pj += 2) {
@@ -426,27 +463,27 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
         process(fb, base_pos + (2 * pj + 2) * kBlk, pool_end);
       }
     } else {
-      // the largest query tiles leave no registers for a second pair in flight
       for (int pj = 0; pj < npairs; ++pj) {
         Frag fa;
         load(fa, pj);
         process(fa, base_pos + 2 * pj * kBlk, pool_end);
       }
     }
-  }
+    cb += 64;
+  } while (cb < nblk);
 
   // Tail step of a fused append: the pairs from pool_end to the end of the
   // partition.  Old rows come from the pool (blocks holding no old row are
   // not read), the rows this launch appends ([n - t_new, n)) from
   // k_new / v_new ([n_seq * t_new][hkv][D], rows of query row q at q * t_new ..).
   if constexpr (FUSED) {
-    const int old_end = u.n - p.t_new;
+    const int old_end = n - p.t_new;
     const size_t rstride = static_cast<size_t>(p.hkv) * D;  // elements between new rows
     const T* kn = static_cast<const T*>(p.app.k_new) + (static_cast<size_t>(u.q_row) * p.t_new * p.hkv + kvh) * D;
     const uint16_t* vn =
         static_cast<const uint16_t*>(p.app.v_new) + (static_cast<size_t>(u.q_row) * p.t_new * p.hkv + kvh) * D;
 #pragma unroll 1
-    for (int pos0 = pool_end; pos0 < u.tok_end; pos0 += 2 * kBlk) {
+    for (int pos0 = pool_end; pos0 < tok_end; pos0 += 2 * kBlk) {
       Frag f;
       const int blk0 = pos0 / kBlk;
       const bool old0 = blk0 * kBlk < old_end;
@@ -468,7 +505,7 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
         f.v1[c] = page_load8<false>(rv1, ((16 * c + col) * kBlk + 4 * grp) * 2);
       }
       // splice in the new rows, one token at a time (selects, no divergent branches)
-      const int i_end = min(pos0 + 2 * kBlk, u.n);
+      const int i_end = min(pos0 + 2 * kBlk, n);
 #pragma unroll 1
       for (int i = max(pos0, old_end); i < i_end; ++i) {
         const int rel = i - pos0;
@@ -500,7 +537,7 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
           }
         }
       }
-      process(f, pos0, u.tok_end);
+      process(f, pos0, tok_end);
     }
   }
 
@@ -560,6 +597,9 @@ __device__ inline void attn_body32(const AttnParams& p, const Unit& u, int kvh) 
   const int grp = lane >> 4;
   const int rows = p.rows;
   const int G = p.group;
+  const Range rg = resolve(p, u, u.n_raw);
+  const int n = rg.n;
+  const int tok_end = rg.tok_end;
 
   f32x4 qv[NT][KS];
   int lim[NT];
@@ -572,11 +612,11 @@ __device__ inline void attn_body32(const AttnParams& p, const Unit& u, int kvh) 
                         (static_cast<size_t>(u.q_row * p.k_draft + i) * p.hq + kvh * G + g) * D;
 #pragma unroll
       for (int s = 0; s < KS; ++s) qv[nt][s] = *reinterpret_cast<const f32x4*>(qp + 16 * s + 4 * grp);
-      lim[nt] = u.n - p.k_draft + i;
+      lim[nt] = n - p.k_draft + i;
     } else {
 #pragma unroll
       for (int s = 0; s < KS; ++s) qv[nt][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-      lim[nt] = u.n - 1;
+      lim[nt] = n - 1;
     }
   }
   f32x4 acc[NT][DC];
@@ -593,8 +633,8 @@ __device__ inline void attn_body32(const AttnParams& p, const Unit& u, int kvh) 
   const size_t page = static_cast<size_t>(D) * kBlk;
   const int32_t* bt = p.block_table + static_cast<size_t>(u.seq) * p.max_blocks;
   const int jb0 = u.tok_begin / kBlk;
-  const int nblk = (u.tok_end + kBlk - 1) / kBlk - jb0;
-  const int mask_from = u.n - p.k_draft;
+  const int nblk = (tok_end + kBlk - 1) / kBlk - jb0;
+  const int mask_from = n - p.k_draft;
 
   for (int cb = 0; cb < nblk; cb += 64) {
     const int cnt = min(64, nblk - cb);
@@ -610,11 +650,11 @@ __device__ inline void attn_body32(const AttnParams& p, const Unit& u, int kvh) 
         kk[s] = *reinterpret_cast<const f32x4*>(kp + ((4 * s + grp) * kBlk + col) * 4);
 #pragma unroll
       for (int c = 0; c < DC; ++c) vv[c] = *reinterpret_cast<const f32x4*>(vp + (16 * c + col) * kBlk + 4 * grp);
-      if (pos0 + kBlk > u.n) {
+      if (pos0 + kBlk > n) {
 #pragma unroll
-        for (int c = 0; c < DC; ++c) vv[c] = mask_v32(vv[c], pos0 + 4 * grp, u.n);
+        for (int c = 0; c < DC; ++c) vv[c] = mask_v32(vv[c], pos0 + 4 * grp, n);
       }
-      const bool need_mask = (pos0 + kBlk - 1 > mask_from) || (pos0 + kBlk > u.tok_end);
+      const bool need_mask = (pos0 + kBlk - 1 > mask_from) || (pos0 + kBlk > tok_end);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
@@ -629,7 +669,7 @@ __device__ inline void attn_body32(const AttnParams& p, const Unit& u, int kvh) 
           x[e] = s4[e] * p.scale_log2;
           if (need_mask) {
             const int pos = pos0 + 4 * grp + e;
-            x[e] = (pos < u.tok_end && pos <= lim[nt]) ? x[e] : kNegInf;
+            x[e] = (pos < tok_end && pos <= lim[nt]) ? x[e] : kNegInf;
           }
         }
         float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
@@ -717,13 +757,15 @@ __device__ inline void attn_unit(const AttnParams& p, const int32_t* meta) {
   u.slot_base = w.slot_base;
   u.nparts = w.nparts;
   u.part = w.part;
-  // the length is bounded by the table row the host allocated
-  // (readfirstlane: the value is wave-uniform, and saying so keeps the page
-  // addresses derived from it in scalar registers)
-  const int n = FUSED ? __builtin_amdgcn_readfirstlane(meta[p.lens_by_row + w.q_row]) : p.seq_len[w.seq];
-  u.n = min(n, p.max_blocks * kBlk);
+  // The length travels as a vector load (then made uniform), so that the
+  // bodies' first loads are issued while it is on its way instead of after it.
+  if constexpr (FUSED) {
+    u.n_raw = meta[p.lens_by_row + w.q_row];
+  } else {
+    const auto lens = page_rsrc(p.seq_len, 0x7ffffff0);
+    u.n_raw = __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(lens, w.seq * 4, 0, 0));
+  }
   u.tok_begin = w.nparts > 1 ? w.part * p.part_tokens : 0;
-  u.tok_end = w.nparts > 1 ? min(u.n, u.tok_begin + p.part_tokens) : u.n;
   if constexpr (std::is_same_v<T, float>)
     attn_body32<D, NT>(p, u, kvh);
   else
@@ -755,19 +797,20 @@ void attn_append_kernel(AttnParams p, InlineMeta im) {
 // per (sequence, key/value head, query row):
 //   M = max_p m_p,  w_p = 2^(m_p - M),  O = sum_p w_p acc_p / sum_p w_p l_p,
 //   lse = (M + log2 sum_p w_p l_p) * ln 2
-// The D/4 16-byte chunks of a row are spread over D/4 threads; the partitions
-// over NG = 1024/D groups of such threads (partition q to group q % NG), so
-// every thread has several independent loads in flight.  Groups are combined
-// in a fixed order, so the result is deterministic.
+// The D/4 16-byte chunks of a row are spread over D/4 threads, the partitions
+// over NG = 1024/D groups of such threads (partition q to group q % NG).  A
+// thread requests the (m, l) pair and the row chunk of all its partitions at
+// once and combines them with a running maximum; the groups are then combined
+// in a fixed order through LDS, so the result is deterministic.
 constexpr int kMergeThreads = 256;
 
 template <typename T, int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
   constexpr int NC = D / 4;                 // float4 chunks per row
   constexpr int NG = kMergeThreads / NC;    // partition groups
-  __shared__ float red[kMergeThreads / 64];
   __shared__ f32x4 part_acc[NG][NC];
-  __shared__ float part_den[NG];
+  __shared__ float part_m[NG];
+  __shared__ float part_l[NG];
   const int tid = threadIdx.x;
   const int rows = p.rows;
   const int r = blockIdx.x % rows;
@@ -778,42 +821,45 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
   const int base = mu.slot_base + kvh * P;
   const float* ml = p.ws_ml + (static_cast<size_t>(base) * rows + r) * 2;  // partition q at ml[q * rows * 2]
   const size_t mstride = static_cast<size_t>(rows) * 2;
-  // block-wide max of m_q
-  float M = kNegInf;
-  for (int q = tid; q < P; q += kMergeThreads) M = fmaxf(M, ml[q * mstride]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  if ((tid & 63) == 0) red[tid >> 6] = M;
-  __syncthreads();
-  M = red[0];
-#pragma unroll
-  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, red[w]);
-  // weighted sums: thread (g, c) takes chunk c of partitions g, g + NG, ...
   const int g = tid / NC;
   const int c = tid - g * NC;
   const f32x4* acc = reinterpret_cast<const f32x4*>(p.ws_acc + (static_cast<size_t>(base) * rows + r) * D) + c;
   const size_t astride = static_cast<size_t>(rows) * D / 4;
+  float mg = kNegInf, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-#pragma unroll 8
+#pragma unroll 4
   for (int q = g; q < P; q += NG) {
-    const float w = __builtin_amdgcn_exp2f(ml[q * mstride] - M);
-    den += w * ml[q * mstride + 1];
+    const float m = ml[q * mstride];
+    const float l = ml[q * mstride + 1];
     const f32x4 a = acc[q * astride];
+    const float mn = fmaxf(mg, m);
+    const float mu_ = (mn == kNegInf) ? 0.f : mn;  // a partition may see no token of a draft row
+    const float so = __builtin_amdgcn_exp2f(mg - mu_);
+    const float sn = __builtin_amdgcn_exp2f(m - mu_);
+    den = den * so + l * sn;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) num[e] += w * a[e];
+    for (int e = 0; e < 4; ++e) num[e] = num[e] * so + a[e] * sn;
+    mg = mn;
   }
   part_acc[g][c] = num;
-  if (c == 0) part_den[g] = den;
+  if (c == 0) {
+    part_m[g] = mg;
+    part_l[g] = den;
+  }
   __syncthreads();
   if (tid < NC) {
-    f32x4 sum = part_acc[0][tid];
-    float dsum = part_den[0];
+    float M = part_m[0];
 #pragma unroll
-    for (int k = 1; k < NG; ++k) {
+    for (int k = 1; k < NG; ++k) M = fmaxf(M, part_m[k]);
+    const float mu_ = (M == kNegInf) ? 0.f : M;
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    float dsum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sum[e] += part_acc[k][tid][e];
-      dsum += part_den[k];
+    for (int k = 0; k < NG; ++k) {
+      const float w = __builtin_amdgcn_exp2f(part_m[k] - mu_);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sum[e] += w * part_acc[k][tid][e];
+      dsum += w * part_l[k];
     }
     const int i = r / p.group, gg = r - (r / p.group) * p.group;
     const size_t orow = static_cast<size_t>(mu.q_row * p.k_draft + i) * p.hq + kvh * p.group + gg;
