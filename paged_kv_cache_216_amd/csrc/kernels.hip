@@ -244,7 +244,7 @@ __device__ inline void store_elem(T* p, float v) {
 // metadata); the bodies resolve the token range from it after their first
 // loads are issued, so that those loads do not wait for the length.
 struct Unit {
-  int q_row, seq, n_raw, tok_begin, slot_base, nparts, part;
+  int q_row, seq, n_raw, tok_begin, slot_base, nparts, part, merge;
 };
 
 struct Range {
@@ -258,6 +258,92 @@ __device__ inline Range resolve(const AttnParams& p, const Unit& u, int n_raw) {
   r.n = min(__builtin_amdgcn_readfirstlane(n_raw), p.max_blocks * kBlk);  // bounded by the table row
   r.tok_end = u.nparts > 1 ? min(r.n, u.tok_begin + p.part_tokens) : r.n;
   return r;
+}
+
+// Device-scope ("sc1") float store and 16-byte load: coherent across XCDs
+// without flushing or invalidating whole L2 caches.
+__device__ inline void store_device(float* a, float v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline float load_device(const float* a) {
+  return __hip_atomic_load(const_cast<float*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kCacheDeviceScope = 16;  // buffer-instruction cache policy: sc1
+
+__device__ inline f32x4 load_device4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCacheDeviceScope));
+}
+
+// Merge of a split (sequence, kv head) inside the attention launch, by the
+// wave whose partition finishes last (rows <= 16, parts <= kInlineMergeParts).
+// Its partial stores are complete (vmcnt 0) before it counts itself in; the
+// wave that counts the last partition reads every partition's (m, l, acc) with
+// device-scope loads and writes out and lse with the same exact formula as
+// merge_kernel, partitions in order:
+//   M = max m_q, w_q = 2^(m_q - M), O = sum w_q acc_q / sum w_q l_q.
+// Rows go in chunks of 4: lane = 16 * row + column group of D / 16 columns.
+template <typename T, int D>
+__device__ inline void merge_last(const AttnParams& p, const Unit& u, int kvh) {
+  constexpr int V = D / 64;  // 16-byte column chunks per lane
+  const int lane = threadIdx.x;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores have completed
+  unsigned* ctr = p.merge_ctr + u.merge * p.hkv + kvh;
+  unsigned old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __builtin_amdgcn_readfirstlane(old);
+  if (old != static_cast<unsigned>(u.nparts - 1)) return;
+  // every partition has counted itself: reset for the next launch, then merge
+  if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int P = u.nparts;
+  const int rows = p.rows;
+  const int base = u.slot_base + kvh * P;
+  const auto racc = page_rsrc(p.ws_acc, 0x7ffffff0);
+  const int c0 = (lane & 15) * (D / 16);
+  for (int r0 = 0; r0 < rows; r0 += 4) {
+    const int r = r0 + (lane >> 4);
+    const int rr = r < rows ? r : rows - 1;
+    float m[kInlineMergeParts], l[kInlineMergeParts];
+    f32x4 a[kInlineMergeParts][V];
+#pragma unroll
+    for (int q = 0; q < kInlineMergeParts; ++q) {
+      const int qq = q < P ? q : P - 1;
+      const size_t sl = static_cast<size_t>(base + qq) * rows + rr;
+      m[q] = load_device(p.ws_ml + 2 * sl);
+      l[q] = load_device(p.ws_ml + 2 * sl + 1);
+#pragma unroll
+      for (int v = 0; v < V; ++v) a[q][v] = load_device4(racc, static_cast<int>((sl * D + c0 + 4 * v) * 4));
+    }
+    float M = m[0];
+#pragma unroll
+    for (int q = 1; q < kInlineMergeParts; ++q) M = q < P ? fmaxf(M, m[q]) : M;
+    const float mu = (M == kNegInf) ? 0.f : M;
+    float den = 0.f;
+    f32x4 num[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) num[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < kInlineMergeParts; ++q) {
+      const float w = q < P ? __builtin_amdgcn_exp2f(m[q] - mu) : 0.f;
+      den += w * l[q];
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) num[v][e] += w * a[q][v][e];
+    }
+    if (r < rows) {
+      const int i = r / p.group, g = r - (r / p.group) * p.group;
+      const size_t orow = static_cast<size_t>(u.q_row * p.k_draft + i) * p.hq + kvh * p.group + g;
+      const float inv = 1.f / den;
+      T* op = static_cast<T*>(p.out) + orow * D + c0;
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store_elem(op + 4 * v + e, num[v][e] * inv);
+      if ((lane & 15) == 0 && p.lse) p.lse[orow] = (M + __builtin_amdgcn_logf(den)) * kLn2;
+    }
+  }
 }
 
 // 16-bit element types: bf16 or f16
@@ -567,6 +653,9 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
             (m_run[nt] + __builtin_amdgcn_logf(l)) * kLn2;
       }
     } else {
+      // single-tile partials may be merged inside this launch: they are stored
+      // at device scope (written through this XCD's L2), so that a merging
+      // wave on another XCD reads them
       const int slot = u.slot_base + kvh * u.nparts + u.part;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -574,16 +663,29 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
         if (r < rows) {
           float* ap = p.ws_acc + (static_cast<size_t>(slot) * rows + r) * D;
 #pragma unroll
-          for (int c = 0; c < DC; ++c) ap[16 * c + col] = acc[nt][c][jj];
+          for (int c = 0; c < DC; ++c) {
+            if constexpr (NT == 1)
+              store_device(ap + 16 * c + col, acc[nt][c][jj]);
+            else
+              ap[16 * c + col] = acc[nt][c][jj];
+          }
         }
       }
       const int r = nt * 16 + col;
       if (grp == 0 && r < rows) {
         float* mp = p.ws_ml + (static_cast<size_t>(slot) * rows + r) * 2;
-        mp[0] = m_run[nt];
-        mp[1] = l;
+        if constexpr (NT == 1) {
+          store_device(mp, m_run[nt]);
+          store_device(mp + 1, l);
+        } else {
+          mp[0] = m_run[nt];
+          mp[1] = l;
+        }
       }
     }
+  }
+  if constexpr (NT == 1) {
+    if (p.inline_merge && u.slot_base >= 0) merge_last<T, D>(p, u, kvh);
   }
 }
 
@@ -757,6 +859,7 @@ __device__ inline void attn_unit(const AttnParams& p, const int32_t* meta) {
   u.slot_base = w.slot_base;
   u.nparts = w.nparts;
   u.part = w.part;
+  u.merge = w.merge;
   // The length travels as a vector load (then made uniform), so that the
   // bodies' first loads are issued while it is on its way instead of after it.
   if constexpr (FUSED) {

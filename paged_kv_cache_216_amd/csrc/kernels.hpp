@@ -48,7 +48,9 @@ struct WorkUnit {
   int32_t part;       // partition index
   int32_t nparts;     // partitions of this sequence (1 = unsplit)
   int32_t slot_base;  // -1: write out/lse directly; else partial slot of kv head 0, part 0
-  int32_t pad0, pad1, pad2;
+  int32_t pad0;       // length at plan time (host-side ordering only)
+  int32_t merge;      // split sequences: index of its MergeUnit; else -1
+  int32_t pad2;
 };
 
 // One split sequence: its partials are merged into out / lse.
@@ -89,7 +91,15 @@ struct AttnParams {
   int lens_by_row;
   int app_blocks;
   AppendParams app;
+  // In-launch merge (inline_merge = 1): the last partition of a split
+  // (sequence, kv head) to finish merges all of them; merge_ctr[merge * hkv +
+  // kvh] counts finished partitions and is zero between launches.  Used when
+  // every split sequence has at most kInlineMergeParts partitions and rows <= 16.
+  unsigned* merge_ctr;
+  int inline_merge;
 };
+
+constexpr int kInlineMergeParts = 8;
 
 hipError_t launch_append(const AppendParams& p, const InlineMeta* meta, hipStream_t stream);
 hipError_t launch_attention(DType dt, const AttnParams& p, const InlineMeta* meta, hipStream_t stream);

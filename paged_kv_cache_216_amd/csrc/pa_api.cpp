@@ -70,6 +70,10 @@ struct pa_pool {
   // cached attention plan in device memory: WorkUnits then MergeUnits
   void* dplan = nullptr;
   size_t dplan_cap = 0;  // bytes
+  // partition counters of the in-launch merge, zero between launches
+  unsigned* merge_ctr = nullptr;
+  size_t merge_ctr_cap = 0;  // counters
+  int plan_max_parts = 0;
   std::vector<int32_t> plan_key, key_scratch;
   int plan_units = 0, plan_merges = 0;
   int64_t plan_slots = 0;
@@ -236,14 +240,15 @@ void make_plan(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt) {
   for (int i = 0; i < n_seq; ++i) {
     const int parts = p->parts[i];
     if (parts == 1) {
-      tail.push_back({i, seq_ids[i], 0, 1, -1, p->lens[i], 0, 0});
+      tail.push_back({i, seq_ids[i], 0, 1, -1, p->lens[i], -1, 0});
       continue;
     }
     const int base = static_cast<int>(slots);
+    const int merge = static_cast<int>(p->merges.size());
     slots += static_cast<int64_t>(parts) * p->hkv;
     for (int q = 0; q < parts; ++q) {
       const int len = std::min(p->lens[i], (q + 1) * pt) - q * pt;
-      (len == pt ? units : tail).push_back({i, seq_ids[i], q, parts, base, len, 0, 0});
+      (len == pt ? units : tail).push_back({i, seq_ids[i], q, parts, base, len, merge, 0});
     }
     p->merges.push_back({i, base, parts, 0});
   }
@@ -253,6 +258,26 @@ void make_plan(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt) {
   });
   units.insert(units.end(), tail.begin(), tail.end());
   p->plan_slots = slots;
+  p->plan_max_parts = 0;
+  for (const pa::MergeUnit& m : p->merges) p->plan_max_parts = std::max(p->plan_max_parts, m.nparts);
+}
+
+// Counters for the in-launch merge: at least n, zeroed when (re)allocated.
+int ensure_merge_ctr(pa_pool* p, size_t n) {
+  if (n <= p->merge_ctr_cap) return PA_OK;
+  const size_t cap = std::max(n, 2 * p->merge_ctr_cap);
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_err(e, "hipDeviceSynchronize");
+  if (p->merge_ctr) hipFree(p->merge_ctr);
+  p->merge_ctr = nullptr;
+  p->merge_ctr_cap = 0;
+  e = hipMalloc(&p->merge_ctr, cap * sizeof(unsigned));
+  if (e != hipSuccess) return hip_err(e, "hipMalloc(merge counters)");
+  e = hipMemset(p->merge_ctr, 0, cap * sizeof(unsigned));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_err(e, "hipMemset(merge counters)");
+  p->merge_ctr_cap = cap;
+  return PA_OK;
 }
 
 size_t plan_ws_bytes(const pa_pool* p, int64_t slots, int rows) {
@@ -410,6 +435,8 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
       rc = release_stage(pst, stream);
       if (rc != PA_OK) return rc;
     }
+    rc = ensure_merge_ctr(p, p->merges.size() * static_cast<size_t>(p->hkv));
+    if (rc != PA_OK) return rc;
     p->plan_key.swap(key);
     p->plan_units = static_cast<int>(p->units.size());
     p->plan_merges = static_cast<int>(p->merges.size());
@@ -442,6 +469,11 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   ak.scale_log2 = scale * 1.4426950408889634f;
   ak.stream_kv = p->bp.num_shared() == 0 ? 1 : 0;
   ak.app = base_append(p);
+  // Short splits (few partitions, one row tile) are merged inside the
+  // attention launch by the last partition to finish; others by merge_kernel.
+  ak.merge_ctr = p->merge_ctr;
+  ak.inline_merge = (p->dtype != PA_F32 && rows <= 16 && p->plan_max_parts <= pa::kInlineMergeParts &&
+                     ws_bytes < (size_t{1} << 31)) ? 1 : 0;
   Stage* st = nullptr;
   if (fused) {
     // metadata: this append's table / length updates, the new rows' slots, and
@@ -469,7 +501,7 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
     if (e != hipSuccess) return hip_err(e, "attention kernel");
     prof_end(p, stream, &ev);
   }
-  if (ak.n_merges > 0) {
+  if (ak.n_merges > 0 && !ak.inline_merge) {
     ProfEvent ev{};
     prof_begin(p, 1, stream, &ev);
     hipError_t e = pa::launch_merge(dt, ak, stream);
@@ -554,10 +586,9 @@ int pa_destroy_pool(pa_pool* p) {
     hipEventDestroy(ev.start);
     hipEventDestroy(ev.stop);
   }
-  if (p->dplan) {
-    hipDeviceSynchronize();
-    hipFree(p->dplan);
-  }
+  if (p->dplan || p->merge_ctr) hipDeviceSynchronize();
+  if (p->dplan) hipFree(p->dplan);
+  if (p->merge_ctr) hipFree(p->merge_ctr);
   delete p;
   return PA_OK;
 }

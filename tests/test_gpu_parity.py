@@ -11,6 +11,7 @@ from gpu_harness import (FILL, Pair, assert_close, contiguous_reference, oracle_
                          to_torch)
 from paged_kv_cache_216_amd import PaInvalid, PaNoMem
 from workloads import make_custom, make_gqa70b, make_highbatch, make_long, make_tiny, make_verify
+from workloads.synth import _to_storage as to_storage
 
 pytestmark = pytest.mark.gpu
 
@@ -26,6 +27,8 @@ def _decode(pair, seqs, q_bits, scale, pt=0, ws=True, k_draft=1):
     if ws:
         workspace = pair.gpu.make_workspace(len(seqs), w.num_q_heads, int(max(pair.model.length(s) for s in seqs)),
                                             k_draft=k_draft, partition_tokens=pt)
+        if workspace is not None:
+            workspace.fill_(float("nan"))  # a partial read before it is written shows up
     if k_draft == 1:
         out, lse = pair.gpu.decode(seqs, q.reshape(len(seqs), w.num_q_heads, w.head_dim).contiguous(), scale,
                                    partition_tokens=pt, workspace=workspace)
@@ -330,6 +333,33 @@ def test_many_partitions_fused_merge_and_repeat():
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16)) and torch.equal(lse, lse2)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_split_merge_reads_this_calls_partials(dtype):
+    """Splits of 2..8 partitions (merged inside the attention launch): three
+    calls on one workspace with different queries each match the oracle, so no
+    call reads partials or counters left by the one before; the third call
+    repeats the first bitwise."""
+    w = make_custom(lengths=[1000, 2048, 300, 700, 90], num_q_heads=16, num_kv_heads=4, head_dim=128,
+                    dtype=dtype, seed=35)
+    pair = Pair(w)
+    pair.fill()
+    seqs = list(range(5))
+    ws = pair.gpu.make_workspace(5, w.num_q_heads, 2048, partition_tokens=256)
+    ws.fill_(float("nan"))
+    rng = np.random.default_rng(36)
+    q2_bits = to_storage(rng.standard_normal(w.q.shape, dtype=np.float32), dtype)
+    outs = []
+    for q_bits in (w.q, q2_bits, w.q):
+        q = to_torch(q_bits, dtype).reshape(5, w.num_q_heads, w.head_dim).contiguous()
+        out, lse = pair.gpu.decode(seqs, q, w.scale, partition_tokens=256, workspace=ws)
+        torch.cuda.synchronize()
+        ro, rl = oracle_decode(pair, seqs, q_bits, w.scale)
+        assert_close(out[:, None], lse[:, None], ro, rl, dtype, "split, in-launch merge")
+        outs.append((out.clone(), lse.clone()))
+    assert torch.equal(outs[0][0].view(torch.int16), outs[2][0].view(torch.int16))
+    assert torch.equal(outs[0][1], outs[2][1])
+
+
 def _fused_vs_separate(w, prefix_fork_partial=False, pending_fork=False):
     """Run the same step as append + attend (two calls) and as one
     pa_append_attend call: pools, tables and outputs must be bitwise equal."""
@@ -348,6 +378,8 @@ def _fused_vs_separate(w, prefix_fork_partial=False, pending_fork=False):
         nv = to_torch(w.new_v.reshape(-1, w.num_kv_heads, w.head_dim), w.dtype)
         q = to_torch(w.q, w.dtype)
         ws = pair.gpu.make_workspace(w.batch, w.num_q_heads, int(w.final_lengths().max()), k_draft=t)
+        if ws is not None:
+            ws.fill_(float("nan"))
         if fused:
             out, lse = pair.gpu.append_attend(seqs, nk, nv, q.contiguous(), w.scale, workspace=ws)
         else:
