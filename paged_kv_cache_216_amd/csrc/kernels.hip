@@ -114,17 +114,21 @@ __device__ inline void append_work(const AppendParams& p, const int32_t* meta, i
   const int h = c / nchunk;
   const int cc = c % nchunk;
   const int slot = meta[p.slots + row];
+  // both 16-byte chunks are read before anything is stored (the stores may
+  // alias the sources as far as the compiler knows, which would serialise them)
+  const u32x4 kv = reinterpret_cast<const u32x4*>(p.k_new)[static_cast<size_t>(row) * chunks_per_row + c];
+  const u32x4 vv = reinterpret_cast<const u32x4*>(p.v_new)[static_cast<size_t>(row) * chunks_per_row + c];
   const int phys = slot / kBlk;
   const int t = slot % kBlk;
-  const u32x4 kv = reinterpret_cast<const u32x4*>(p.k_new)[static_cast<size_t>(row) * chunks_per_row + c];
   u32x4* kdst = reinterpret_cast<u32x4*>(p.k_pool) +
                 ((static_cast<size_t>(phys) * p.hkv + h) * nchunk + cc) * kBlk + t;
   *kdst = kv;
-  const Elem* vsrc = reinterpret_cast<const Elem*>(p.v_new) + (static_cast<size_t>(row) * chunks_per_row + c) * X;
+  // V: the chunk's X consecutive dims go to X dims of the slot, kBlk apart
   Elem* vdst = reinterpret_cast<Elem*>(p.v_pool) + (static_cast<size_t>(phys) * p.hkv + h) * page +
                static_cast<size_t>(cc) * X * kBlk + t;
+  const auto ve = __builtin_bit_cast(Elem __attribute__((ext_vector_type(X))), vv);
 #pragma unroll
-  for (int i = 0; i < X; ++i) vdst[i * kBlk] = vsrc[i];
+  for (int i = 0; i < X; ++i) vdst[i * kBlk] = ve[i];
 }
 
 template <int E>
@@ -498,9 +502,12 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
   // nothing in it waits on the length before its table entries are requested;
   // with no block in range every load below reads zero and touches no memory)
   int cb = 0;
+  int tb_cur = 0, cb_cur = 0;  // the last chunk processed, kept for the tail step
   do {
     const int cnt = max(0, min(64, nblk - cb));
     const int tb = tb_next;
+    tb_cur = tb;
+    cb_cur = cb;
     tb_next = __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(trow, (jb0 + cb + 64 + lane) * 4, 0, 0));
     const int npairs = (cnt + 1) >> 1;
     // a table entry outside the pool can only come from a host-side bug; clamp
@@ -574,8 +581,14 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       const int blk0 = pos0 / kBlk;
       const bool old0 = blk0 * kBlk < old_end;
       const bool old1 = (blk0 + 1) * kBlk < old_end;
-      const int phys0 = old0 ? min(max(bt[blk0], 0), p.num_blocks - 1) : 0;
-      const int phys1 = old1 ? min(max(bt[blk0 + 1], 0), p.num_blocks - 1) : 0;
+      // table entries: from the chunks already in registers when they hold them
+      auto entry = [&](int blk) {
+        const int j = blk - jb0 - cb_cur;
+        const int e = j < 64 ? readlane(tb_cur, j & 63) : (j < 128 ? readlane(tb_next, j & 63) : bt[blk]);
+        return min(max(e, 0), p.num_blocks - 1);
+      };
+      const int phys0 = old0 ? entry(blk0) : 0;
+      const int phys1 = old1 ? entry(blk0 + 1) : 0;
       const size_t off0 = (static_cast<size_t>(phys0) * p.hkv + kvh) * page;
       const size_t off1 = (static_cast<size_t>(phys1) * p.hkv + kvh) * page;
       const auto rk0 = page_rsrc(kpool + off0, old0 ? kPageBytes : 0), rv0 = page_rsrc(vpool + off0, old0 ? kPageBytes : 0);
@@ -590,36 +603,41 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
         f.v0[c] = page_load8<false>(rv0, ((16 * c + col) * kBlk + 4 * grp) * 2);
         f.v1[c] = page_load8<false>(rv1, ((16 * c + col) * kBlk + 4 * grp) * 2);
       }
-      // splice in the new rows, one token at a time (selects, no divergent branches)
+      // splice in the new rows, one token at a time: the row's loads are all
+      // issued before any is used, and the splice is selects only
       const int i_end = min(pos0 + 2 * kBlk, n);
 #pragma unroll 1
       for (int i = max(pos0, old_end); i < i_end; ++i) {
         const int rel = i - pos0;
-        const int b = rel >> 4;
+        const bool in0 = rel < kBlk;
         const int t = rel & 15;
         const size_t row = static_cast<size_t>(i - old_end) * rstride;
+        Op x[KS];
+        uint16_t nv[DC];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) x[s] = __builtin_bit_cast(Op, *reinterpret_cast<const u32x4*>(kn + row + 32 * s + 8 * grp));
+#pragma unroll
+        for (int c = 0; c < DC; ++c) nv[c] = vn[row + 16 * c + col];
         const bool kl = col == t;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          const Op x = __builtin_bit_cast(Op, *reinterpret_cast<const u32x4*>(kn + row + 32 * s + 8 * grp));
-          if (b == 0)
-            f.k0[s] = kl ? x : f.k0[s];
-          else
-            f.k1[s] = kl ? x : f.k1[s];
+          f.k0[s] = (kl && in0) ? x[s] : f.k0[s];
+          f.k1[s] = (kl && !in0) ? x[s] : f.k1[s];
         }
+        // V: lane (col, grp) holds tokens 4 grp .. 4 grp + 3 of dim 16 c + col,
+        // two per 32-bit word
         const bool vl = grp == (t >> 2);
         const int word = (t & 3) >> 1;
         const int shift = (t & 1) * 16;
         const uint32_t keep = ~(0xFFFFu << shift);
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
-          const uint32_t bits = static_cast<uint32_t>(vn[row + 16 * c + col]) << shift;
-          if (b == 0) {
-            const uint32_t w = (f.v0[c][word] & keep) | bits;
-            f.v0[c][word] = vl ? w : f.v0[c][word];
-          } else {
-            const uint32_t w = (f.v1[c][word] & keep) | bits;
-            f.v1[c][word] = vl ? w : f.v1[c][word];
+          const uint32_t bits = static_cast<uint32_t>(nv[c]) << shift;
+#pragma unroll
+          for (int wi = 0; wi < 2; ++wi) {
+            const bool hit = vl && word == wi;
+            f.v0[c][wi] = (hit && in0) ? ((f.v0[c][wi] & keep) | bits) : f.v0[c][wi];
+            f.v1[c][wi] = (hit && !in0) ? ((f.v1[c][wi] & keep) | bits) : f.v1[c][wi];
           }
         }
       }
