@@ -311,7 +311,7 @@ def main():
     # Kernel durations: the same K steps again with the library's HIP events
     # recorded around every launch on the launch stream (events between the
     # kernels stretch the step, so the step time above is taken without them).
-    kern = {0: [0.0, 0], 1: [0.0, 0], 2: [0.0, 0]}
+    kern = {0: [0.0, 0], 1: [0.0, 0], 2: [0.0, 0], 3: [0.0, 0]}
     if not args.no_profile_events:
         for r in reps:
             for k in kern:
@@ -326,6 +326,19 @@ def main():
                 ms, n = r.cache.profile_read(k)
                 kern[k][0] += ms
                 kern[k][1] += n
+    # Per-step distribution: one more pass with an event pair around each step
+    # (a step's own events add a little to it).
+    pct = None
+    if not args.no_profile_events:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i in range(args.steps):
+            evs[i][0].record(stream)
+            reps[i % len(reps)].step(sh)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        st = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+        pct = {"p50": round(float(np.percentile(st, 50)), 2), "p90": round(float(np.percentile(st, 90)), 2),
+               "p99": round(float(np.percentile(st, 99)), 2), "mean": round(float(st.mean()), 2)}
     dec_b = decode_bytes(w)
     app_b = append_bytes(w)
     step_b = dec_b + app_b
@@ -353,7 +366,9 @@ def main():
                    "cached_tokens": int(sum(step_lengths(w)))},
         "kernel_us": {"attention": round(1e3 * kern[0][0] / max(1, kern[0][1]), 2),
                       "merge": round(1e3 * kern[1][0] / max(1, kern[1][1]), 2) if kern[1][1] else None,
-                      "append": round(1e3 * kern[2][0] / max(1, kern[2][1]), 2) if kern[2][1] else None},
+                      "append": round(1e3 * kern[2][0] / max(1, kern[2][1]), 2) if kern[2][1] else None,
+                      "shared_prefix": round(1e3 * kern[3][0] / max(1, kern[3][1]), 2) if kern[3][1] else None},
+        "step_us_percentiles": pct,
         "host_wall_ms_per_step": round(1e3 * wall / args.steps, 4),
         "host_enqueue_us_per_step": round(1e6 * t_enq / args.steps, 2),
         "step_calls": "pa_append_attend" if fused else ("pa_append_kv + attention" if reps[0].t_new else "attention"),

@@ -130,6 +130,16 @@ int pa_append_kv(pa_pool* pool, const int32_t* seq_ids, int n_seq, const int32_t
  *                pa_workspace_size); may be NULL when no sequence is split.
  *                With partition_tokens = 0 the library only splits when the
  *                workspace is large enough.
+ * Shared prefixes: when at least 4 sequences of the call are copy-on-write
+ * forks whose first partitions (whole partitions that every query row sees)
+ * sit in the same physical blocks, those partitions are computed once for the
+ * query rows of all of them, in a launch before the attention launch, so the
+ * shared blocks are read once per call instead of once per sequence (blocks
+ * shared by sequences of one prompt: "PagedAttention, décodage spéculatif,
+ * MoE et Blackwell", section 1; kenji.blog page, section 4.2; reusing the KV
+ * cache of a common prefix: ranksignal.fr post 218, "Mettre en cache").
+ * Needs the split (a workspace) and a 16-bit dtype.  Results equal the
+ * per-sequence computation up to floating-point summation order.
  * Softmax and accumulation are fp32; out is rounded to dtype (nearest even). */
 int pa_decode(pa_pool* pool, const int32_t* seq_ids, int n_seq, int num_q_heads, float scale,
               const void* q, void* out, float* lse, int partition_tokens, void* workspace,
@@ -202,7 +212,7 @@ const char* pa_last_error(void);
  * synchronises those events and returns the summed elapsed milliseconds and
  * the number of launches since the last read (then resets).
  * which: 0 = attention kernel (decode / verify), 1 = split merge kernel,
- *        2 = append kernel. */
+ *        2 = append kernel, 3 = shared-prefix kernel. */
 int pa_profile_enable(pa_pool* pool, int on);
 int pa_profile_read(pa_pool* pool, int which, double* total_ms, int64_t* launches);
 

@@ -248,7 +248,8 @@ __device__ inline void store_elem(T* p, float v) {
 // metadata); the bodies resolve the token range from it after their first
 // loads are issued, so that those loads do not wait for the length.
 struct Unit {
-  int q_row, seq, n_raw, tok_begin, slot_base, nparts, part, merge;
+  int q_row, seq, n_raw, tok_begin, slot_base, nparts, part, merge, nlaunch;
+  int pre_row0, pre_member0, pre_rows;  // shared-prefix pass only
 };
 
 struct Range {
@@ -297,7 +298,7 @@ __device__ inline void merge_last(const AttnParams& p, const Unit& u, int kvh) {
   unsigned old = 0;
   if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = __builtin_amdgcn_readfirstlane(old);
-  if (old != static_cast<unsigned>(u.nparts - 1)) return;
+  if (old != static_cast<unsigned>(u.nlaunch - 1)) return;  // (earlier partitions: a previous launch)
   // every partition has counted itself: reset for the next launch, then merge
   if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int P = u.nparts;
@@ -351,13 +352,13 @@ __device__ inline void merge_last(const AttnParams& p, const Unit& u, int kvh) {
 }
 
 // 16-bit element types: bf16 or f16
-template <typename T, int D, int NT, bool NTL, bool FUSED>
+template <typename T, int D, int NT, bool NTL, bool FUSED, bool PREFIX = false>
 __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) {
   using Op = typename MfmaOp<T>::type;
   constexpr int KS = D / 32;  // QK k-steps per block
   constexpr int DC = D / 16;  // output dim chunks
   constexpr int kPageBytes = D * kBlk * static_cast<int>(sizeof(T));
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;  // one wave; the shared-prefix pass runs several per workgroup
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int rows = p.rows;
@@ -374,12 +375,21 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
   // past the row read as zero, entries past the unit are never used).  Tile
   // rows past `rows` repeat the last query row: their softmax is computed and
   // dropped, and it does not touch the other rows.
+  // (Shared-prefix pass: tile row r is row r % rows of member r / rows.)
   Op qop[NT][KS];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int rr = min(nt * 16 + col, rows - 1);
+    int q_row = u.q_row, rr;
+    if constexpr (PREFIX) {
+      const int r = min(u.pre_row0 + nt * 16 + col, u.pre_rows - 1);
+      const int j = r / rows;
+      rr = r - j * rows;
+      q_row = p.pre_members[u.pre_member0 + j].q_row;
+    } else {
+      rr = min(nt * 16 + col, rows - 1);
+    }
     const int i = rr / G, g = rr - i * G;
-    const T* qp = static_cast<const T*>(p.q) + (static_cast<size_t>(u.q_row * p.k_draft + i) * p.hq + kvh * G + g) * D;
+    const T* qp = static_cast<const T*>(p.q) + (static_cast<size_t>(q_row * p.k_draft + i) * p.hq + kvh * G + g) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       qop[nt][s] = __builtin_bit_cast(Op, *reinterpret_cast<const u32x4*>(qp + 32 * s + 8 * grp));
@@ -398,7 +408,8 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = nt * 16 + col;
-    lim[nt] = n - p.k_draft + min(r, rows - 1) / G;
+    // a shared prefix lies before every draft's first position: no causal limit
+    lim[nt] = PREFIX ? 0x7fffffff : n - p.k_draft + min(r, rows - 1) / G;
   }
 
   f32x4 acc[NT][DC];
@@ -411,7 +422,7 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
     for (int c = 0; c < DC; ++c) acc[nt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int mask_from = n - p.k_draft;  // positions above this may be masked for some row
+  const int mask_from = PREFIX ? 0x7fffffff : n - p.k_draft;  // positions above this may be masked for some row
   // Rows appended by this very launch (fused append) are not read from the
   // pool, which other workgroups of the launch are writing: the pool pass stops
   // at the last pair boundary before them, and a tail step processes the
@@ -646,6 +657,35 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
   }
 
   // ---- epilogue
+  if constexpr (PREFIX) {
+    // each row's partial goes to partition u.part of its own sequence
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float l = wave_sum_groups(l_run[nt]);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = u.pre_row0 + nt * 16 + 4 * grp + jj;
+        if (r < u.pre_rows) {
+          const int j = r / rows;
+          const PrefixMember m = p.pre_members[u.pre_member0 + j];
+          const int slot = m.slot_base + kvh * m.nparts + u.part;
+          float* ap = p.ws_acc + (static_cast<size_t>(slot) * rows + (r - j * rows)) * D;
+#pragma unroll
+          for (int c = 0; c < DC; ++c) ap[16 * c + col] = acc[nt][c][jj];
+        }
+      }
+      const int r = u.pre_row0 + nt * 16 + col;
+      if (grp == 0 && r < u.pre_rows) {
+        const int j = r / rows;
+        const PrefixMember m = p.pre_members[u.pre_member0 + j];
+        const int slot = m.slot_base + kvh * m.nparts + u.part;
+        float* mp = p.ws_ml + (static_cast<size_t>(slot) * rows + (r - j * rows)) * 2;
+        mp[0] = m_run[nt];
+        mp[1] = l;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const float l = wave_sum_groups(l_run[nt]);
@@ -878,6 +918,7 @@ __device__ inline void attn_unit(const AttnParams& p, const int32_t* meta) {
   u.nparts = w.nparts;
   u.part = w.part;
   u.merge = w.merge;
+  u.nlaunch = w.nlaunch;
   // The length travels as a vector load (then made uniform), so that the
   // bodies' first loads are issued while it is on its way instead of after it.
   if constexpr (FUSED) {
@@ -912,6 +953,39 @@ void attn_append_kernel(AttnParams p, InlineMeta im) {
     return;
   }
   attn_unit<T, D, NT, NTL, true>(p, meta);
+}
+
+// Shared-prefix pass: one workgroup of W waves per (prefix unit, kv head);
+// wave w takes 16 * NT query rows of one group of sequences over one
+// partition of their common prefix.  (Measured on MI355X: 2 tiles per wave
+// with the next pair in flight is best; several waves per workgroup reading
+// the same pages, or 4 tiles per wave, are not faster.)
+template <int D>
+struct PrefixShape {
+  static constexpr int NT = D <= 128 ? 2 : 1;  // row tiles per wave
+  static constexpr int W = 1;                  // waves per workgroup
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(64 * PrefixShape<D>::W) void prefix_kernel(AttnParams p) {
+  constexpr int NT = PrefixShape<D>::NT;
+  const int unit = blockIdx.x / p.hkv;
+  const int kvh = blockIdx.x - unit * p.hkv;
+  const PrefixUnit pu = p.pre_units[unit];
+  const int row0 = pu.row0 + static_cast<int>(threadIdx.x >> 6) * 16 * NT;
+  if (row0 >= pu.group_rows) return;  // whole wave past the group's rows
+  Unit u{};
+  u.seq = pu.seq;
+  u.n_raw = pu.prefix_tokens;
+  u.part = pu.part;
+  u.tok_begin = pu.part * p.part_tokens;
+  u.nparts = 2;  // a partition: tokens [tok_begin, min(prefix, tok_begin + part_tokens))
+  u.slot_base = 0;
+  u.pre_row0 = row0;
+  u.pre_member0 = pu.member0;
+  u.pre_rows = pu.group_rows;
+  // the prefix blocks are read by every row block of the group: cached loads
+  attn_body16<T, D, NT, false, false, true>(p, u, kvh);
 }
 
 // Exact merge of one output row of a split sequence, one 256-thread workgroup
@@ -1034,6 +1108,41 @@ hipError_t launch_attn_t(const AttnParams& p, const InlineMeta& m, hipStream_t s
 }  // namespace
 
 int max_rows_for_head_dim(int head_dim) { return head_dim <= 128 ? 64 : 32; }
+
+int prefix_rows_per_unit(int head_dim) {
+  switch (head_dim) {
+    case 64: return 16 * PrefixShape<64>::NT * PrefixShape<64>::W;
+    case 128: return 16 * PrefixShape<128>::NT * PrefixShape<128>::W;
+    default: return 16 * PrefixShape<256>::NT * PrefixShape<256>::W;
+  }
+}
+
+hipError_t launch_prefix(DType dt, const AttnParams& p, hipStream_t stream) {
+  if (p.n_pre_units == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(p.n_pre_units) * p.hkv);
+  auto go = [&](auto kern, int waves) {
+    hipLaunchKernelGGL(kern, grid, dim3(64 * waves), 0, stream, p);
+    return hipGetLastError();
+  };
+  switch (dt) {
+    case kBF16:
+      switch (p.head_dim) {
+        case 64: return go(prefix_kernel<__bf16, 64>, PrefixShape<64>::W);
+        case 128: return go(prefix_kernel<__bf16, 128>, PrefixShape<128>::W);
+        case 256: return go(prefix_kernel<__bf16, 256>, PrefixShape<256>::W);
+      }
+      break;
+    case kF16:
+      switch (p.head_dim) {
+        case 64: return go(prefix_kernel<_Float16, 64>, PrefixShape<64>::W);
+        case 128: return go(prefix_kernel<_Float16, 128>, PrefixShape<128>::W);
+        case 256: return go(prefix_kernel<_Float16, 256>, PrefixShape<256>::W);
+      }
+      break;
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
 
 int append_blocks64(const AppendParams& p) {
   const AppendGrid g = append_grid(p, 64);

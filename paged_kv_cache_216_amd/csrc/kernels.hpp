@@ -50,7 +50,32 @@ struct WorkUnit {
   int32_t slot_base;  // -1: write out/lse directly; else partial slot of kv head 0, part 0
   int32_t pad0;       // length at plan time (host-side ordering only)
   int32_t merge;      // split sequences: index of its MergeUnit; else -1
-  int32_t pad2;
+  int32_t nlaunch;    // partitions of this sequence computed by this launch (the
+                      // others, if any, by the shared-prefix pass before it)
+};
+
+// Shared-prefix pass.  Sequences of a batch that are copy-on-write forks of
+// one prefix read the same physical blocks for its first `prefix_tokens`
+// tokens (a multiple of the partition length).  The pass computes those
+// partitions once for the query rows of all such sequences together -- up to
+// 64 rows per wave instead of one sequence's G * k_draft -- and writes each
+// row's partial into the slot of its own sequence's partition; the sequence's
+// later partitions and the merge are the usual ones.
+struct PrefixMember {
+  int32_t q_row;      // index of the sequence in q / out
+  int32_t slot_base;  // its partial slot of kv head 0, part 0
+  int32_t nparts;     // its partitions
+  int32_t pad;
+};
+
+struct PrefixUnit {
+  int32_t seq;            // a member's table row (the prefix blocks are the same in all)
+  int32_t part;           // partition of the prefix
+  int32_t row0;           // first row of the group's rows (member * rows + row) for this wave
+  int32_t member0;        // the group's first entry in the member array
+  int32_t group_rows;     // members * rows
+  int32_t prefix_tokens;
+  int32_t pad0, pad1;
 };
 
 // One split sequence: its partials are merged into out / lse.
@@ -97,6 +122,10 @@ struct AttnParams {
   // every split sequence has at most kInlineMergeParts partitions and rows <= 16.
   unsigned* merge_ctr;
   int inline_merge;
+  // shared-prefix pass (launch_prefix)
+  const PrefixUnit* pre_units;
+  const PrefixMember* pre_members;
+  int n_pre_units;
 };
 
 constexpr int kInlineMergeParts = 8;
@@ -104,6 +133,10 @@ constexpr int kInlineMergeParts = 8;
 hipError_t launch_append(const AppendParams& p, const InlineMeta* meta, hipStream_t stream);
 hipError_t launch_attention(DType dt, const AttnParams& p, const InlineMeta* meta, hipStream_t stream);
 hipError_t launch_merge(DType dt, const AttnParams& p, hipStream_t stream);
+// The shared-prefix pass (16-bit dtypes); run before launch_attention.
+hipError_t launch_prefix(DType dt, const AttnParams& p, hipStream_t stream);
+// Query rows one workgroup of the shared-prefix pass takes, for a head dim.
+int prefix_rows_per_unit(int head_dim);
 // Workgroups of 64 threads that the append work of `p` needs.
 int append_blocks64(const AppendParams& p);
 // Largest supported rows (group * k_draft) for a head dim.

@@ -84,6 +84,12 @@ struct pa_pool {
   std::vector<pa::WorkUnit> units, tail_units;
   std::vector<pa::MergeUnit> merges;
   std::vector<int> lens, parts;
+  // shared-prefix pass: partitions of each sequence done by the pass (0 = none)
+  std::vector<int> pre_parts;
+  std::vector<std::pair<int32_t, int>> pre_scratch;
+  std::vector<pa::PrefixUnit> pre_units;
+  std::vector<pa::PrefixMember> pre_members;
+  int plan_pre_units = 0;
   std::vector<int32_t> ntok;
   // call metadata being assembled, and its kernel-argument copy
   std::vector<int32_t> meta;
@@ -91,8 +97,8 @@ struct pa_pool {
   // profiling
   bool prof = false;
   std::vector<ProfEvent> prof_events;
-  double prof_ms[3] = {0, 0, 0};
-  int64_t prof_n[3] = {0, 0, 0};
+  double prof_ms[4] = {0, 0, 0, 0};
+  int64_t prof_n[4] = {0, 0, 0, 0};
 };
 
 namespace {
@@ -230,7 +236,7 @@ int64_t count_parts(pa_pool* p, int n_seq, int pt) {
 // sequences get consecutive partial slots (kv head major within a sequence).
 // Full-length units first, then the rest longest first (by the lengths at plan
 // time), so the grid's tail holds the short ones.
-void make_plan(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt) {
+void make_plan(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, int rows) {
   std::vector<pa::WorkUnit>& units = p->units;
   std::vector<pa::WorkUnit>& tail = p->tail_units;
   units.clear();
@@ -240,15 +246,16 @@ void make_plan(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt) {
   for (int i = 0; i < n_seq; ++i) {
     const int parts = p->parts[i];
     if (parts == 1) {
-      tail.push_back({i, seq_ids[i], 0, 1, -1, p->lens[i], -1, 0});
+      tail.push_back({i, seq_ids[i], 0, 1, -1, p->lens[i], -1, 1});
       continue;
     }
     const int base = static_cast<int>(slots);
     const int merge = static_cast<int>(p->merges.size());
+    const int q0 = p->pre_parts[i];  // partitions done by the shared-prefix pass
     slots += static_cast<int64_t>(parts) * p->hkv;
-    for (int q = 0; q < parts; ++q) {
+    for (int q = q0; q < parts; ++q) {
       const int len = std::min(p->lens[i], (q + 1) * pt) - q * pt;
-      (len == pt ? units : tail).push_back({i, seq_ids[i], q, parts, base, len, merge, 0});
+      (len == pt ? units : tail).push_back({i, seq_ids[i], q, parts, base, len, merge, parts - q0});
     }
     p->merges.push_back({i, base, parts, 0});
   }
@@ -260,6 +267,77 @@ void make_plan(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt) {
   p->plan_slots = slots;
   p->plan_max_parts = 0;
   for (const pa::MergeUnit& m : p->merges) p->plan_max_parts = std::max(p->plan_max_parts, m.nparts);
+
+  // shared-prefix pass: members in batch order per group, one unit per
+  // (group, prefix partition, block of rows)
+  p->pre_units.clear();
+  p->pre_members.clear();
+  std::vector<int> merge_of(n_seq, -1);
+  for (size_t m = 0; m < p->merges.size(); ++m) merge_of[p->merges[m].q_row] = static_cast<int>(m);
+  const auto& pairs = p->pre_scratch;  // (group key, batch index) sorted, prefix sequences only
+  const int rpw = pa::prefix_rows_per_unit(p->head_dim);
+  for (size_t a = 0; a < pairs.size();) {
+    size_t b = a;
+    while (b < pairs.size() && pairs[b].first == pairs[a].first) ++b;
+    const int member0 = static_cast<int>(p->pre_members.size());
+    for (size_t k = a; k < b; ++k) {
+      const pa::MergeUnit& mu = p->merges[merge_of[pairs[k].second]];
+      p->pre_members.push_back({pairs[k].second, mu.slot_base, mu.nparts, 0});
+    }
+    const int first = pairs[a].second;
+    const int q_parts = p->pre_parts[first];
+    const int group_rows = static_cast<int>(b - a) * rows;
+    for (int q = 0; q < q_parts; ++q)
+      for (int r0 = 0; r0 < group_rows; r0 += rpw)
+        p->pre_units.push_back({seq_ids[first], q, r0, member0, group_rows, q_parts * pt, 0, 0});
+    a = b;
+  }
+}
+
+// Groups of copy-on-write forks in the batch whose first partitions sit in the
+// same physical blocks: at least kPrefixMinGroup sequences sharing at least
+// one whole partition that every query row sees (all drafts included).  Sets
+// pre_parts[i] (0 for sequences outside any group) and pre_scratch (group key,
+// batch index), sorted by group.
+constexpr int kPrefixMinGroup = 4;
+
+void find_prefix_groups(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, int k_draft) {
+  p->pre_parts.assign(n_seq, 0);
+  auto& pairs = p->pre_scratch;
+  pairs.clear();
+  if (pt <= 0 || p->dtype == PA_F32 || n_seq < kPrefixMinGroup) return;
+  for (int i = 0; i < n_seq; ++i) {
+    const std::vector<int32_t>& tab = p->bp.table(seq_ids[i]);
+    if (p->lens[i] - k_draft >= pt && !tab.empty() && p->bp.refcount(tab[0]) > 1) pairs.push_back({tab[0], i});
+  }
+  std::sort(pairs.begin(), pairs.end());
+  size_t out = 0;
+  for (size_t a = 0; a < pairs.size();) {
+    size_t b = a;
+    while (b < pairs.size() && pairs[b].first == pairs[a].first) ++b;
+    if (b - a >= static_cast<size_t>(kPrefixMinGroup)) {
+      // tokens every member holds in the same blocks and every query row sees
+      int limit = 1 << 30;
+      for (size_t k = a; k < b; ++k) limit = std::min(limit, p->lens[pairs[k].second] - k_draft);
+      const std::vector<int32_t>& t0 = p->bp.table(seq_ids[pairs[a].second]);
+      int blocks = limit / pa::kBlock;
+      for (size_t k = a + 1; k < b && blocks > 0; ++k) {
+        const std::vector<int32_t>& tk = p->bp.table(seq_ids[pairs[k].second]);
+        int j = 0;
+        while (j < blocks && tk[j] == t0[j]) ++j;
+        blocks = j;
+      }
+      const int q_parts = std::min(blocks * pa::kBlock, limit) / pt;
+      if (q_parts > 0) {
+        for (size_t k = a; k < b; ++k) {
+          p->pre_parts[pairs[k].second] = q_parts;
+          pairs[out++] = pairs[k];
+        }
+      }
+    }
+    a = b;
+  }
+  pairs.resize(out);
 }
 
 // Counters for the in-launch merge: at least n, zeroed when (re)allocated.
@@ -412,24 +490,34 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
     if (rc != PA_OK) return rc;
   }
 
-  // reuse the device plan when the batch and its partition structure are unchanged
+  // forks sharing a prefix: its partitions are computed once for all of them
+  find_prefix_groups(p, seq_ids, n_seq, pt, k_draft);
+
+  // reuse the device plan when the batch, its partition structure and the
+  // shared-prefix grouping are unchanged
   std::vector<int32_t>& key = p->key_scratch;
-  key.assign({pt, n_seq});
+  key.assign({pt, n_seq, rows});
   for (int i = 0; i < n_seq; ++i) {
     key.push_back(seq_ids[i]);
     key.push_back(p->parts[i]);
+    key.push_back(p->pre_parts[i]);
   }
   if (key != p->plan_key) {
-    make_plan(p, seq_ids, n_seq, pt);
-    const size_t plan_words = 8 * p->units.size() + 4 * p->merges.size();
+    make_plan(p, seq_ids, n_seq, pt, rows);
+    const size_t w_units = 8 * p->units.size(), w_merges = 4 * p->merges.size();
+    const size_t w_pre = 8 * p->pre_units.size(), w_mem = 4 * p->pre_members.size();
+    const size_t plan_words = w_units + w_merges + w_pre + w_mem;
     int rc = ensure_dplan(p, plan_words * sizeof(int32_t));
     if (rc != PA_OK) return rc;
     if (plan_words) {
       Stage* pst = nullptr;
       rc = acquire_stage(p, plan_words, &pst);
       if (rc != PA_OK) return rc;
-      std::memcpy(pst->host, p->units.data(), 8 * p->units.size() * sizeof(int32_t));
-      std::memcpy(pst->host + 8 * p->units.size(), p->merges.data(), 4 * p->merges.size() * sizeof(int32_t));
+      int32_t* h = pst->host;
+      std::memcpy(h, p->units.data(), w_units * sizeof(int32_t));
+      std::memcpy(h + w_units, p->merges.data(), w_merges * sizeof(int32_t));
+      std::memcpy(h + w_units + w_merges, p->pre_units.data(), w_pre * sizeof(int32_t));
+      std::memcpy(h + w_units + w_merges + w_pre, p->pre_members.data(), w_mem * sizeof(int32_t));
       hipError_t e = hipMemcpyAsync(p->dplan, pst->host, plan_words * sizeof(int32_t), hipMemcpyHostToDevice, stream);
       if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync(plan)");
       rc = release_stage(pst, stream);
@@ -440,6 +528,7 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
     p->plan_key.swap(key);
     p->plan_units = static_cast<int>(p->units.size());
     p->plan_merges = static_cast<int>(p->merges.size());
+    p->plan_pre_units = static_cast<int>(p->pre_units.size());
   }
 
   pa::AttnParams ak{};
@@ -457,7 +546,12 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   ak.ws_acc = ws;
   ak.ws_ml = ws ? ws + static_cast<size_t>(slots) * rows * p->head_dim : nullptr;
   ak.units = static_cast<const pa::WorkUnit*>(p->dplan);
-  ak.merges = reinterpret_cast<const pa::MergeUnit*>(static_cast<const int32_t*>(p->dplan) + 8 * p->plan_units);
+  const int32_t* dplan = static_cast<const int32_t*>(p->dplan);
+  ak.merges = reinterpret_cast<const pa::MergeUnit*>(dplan + 8 * p->plan_units);
+  ak.pre_units = reinterpret_cast<const pa::PrefixUnit*>(dplan + 8 * p->plan_units + 4 * p->plan_merges);
+  ak.pre_members = reinterpret_cast<const pa::PrefixMember*>(dplan + 8 * p->plan_units + 4 * p->plan_merges +
+                                                             8 * p->plan_pre_units);
+  ak.n_pre_units = p->plan_pre_units;
   ak.n_units = p->plan_units;
   ak.n_merges = p->plan_merges;
   ak.hkv = p->hkv;
@@ -494,6 +588,13 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
     if (rc != PA_OK) return rc;
   }
   const pa::DType dt = static_cast<pa::DType>(p->dtype);
+  if (ak.n_pre_units > 0) {
+    ProfEvent ev{};
+    prof_begin(p, 3, stream, &ev);
+    hipError_t e = pa::launch_prefix(dt, ak, stream);
+    if (e != hipSuccess) return hip_err(e, "shared-prefix kernel");
+    prof_end(p, stream, &ev);
+  }
   if (ak.n_units > 0 || fused) {
     ProfEvent ev{};
     prof_begin(p, 0, stream, &ev);
@@ -736,7 +837,7 @@ int pa_profile_enable(pa_pool* p, int on) {
 }
 
 int pa_profile_read(pa_pool* p, int which, double* total_ms, int64_t* launches) {
-  if (!p || which < 0 || which > 2) return set_err(PA_ERR_INVALID, "bad arguments");
+  if (!p || which < 0 || which > 3) return set_err(PA_ERR_INVALID, "bad arguments");
   for (ProfEvent& ev : p->prof_events) {
     hipError_t e = hipEventSynchronize(ev.stop);
     if (e != hipSuccess) return hip_err(e, "hipEventSynchronize(profile)");

@@ -360,6 +360,51 @@ def test_split_merge_reads_this_calls_partials(dtype):
     assert torch.equal(outs[0][1], outs[2][1])
 
 
+@pytest.mark.parametrize("prefix_len,k_draft,dtype", [(1100, 5, "bf16"), (1024, 1, "f16"), (2100, 3, "bf16")])
+def test_shared_prefix_pass(prefix_len, k_draft, dtype):
+    """Six forks of one prefix: the whole partitions of the prefix (512 tokens
+    each) are computed once for all six in the shared-prefix launch, the rest
+    per sequence; the result matches the oracle and a pool where each sequence
+    holds a private copy of the prefix (no sharing, so no shared-prefix pass)."""
+    _say(f"shared-prefix pass prefix={prefix_len} k={k_draft} {dtype}")
+    w = make_custom(lengths=[16, 77, 200, 512, 31, 100], mode="verify", num_q_heads=16, num_kv_heads=4,
+                    head_dim=128, dtype=dtype, seed=37, k_draft=k_draft, prefix_len=prefix_len)
+    shared = Pair(w)
+    shared.fill()
+    shared.append_step_rows()
+    seqs = list(range(w.batch))
+    shared.gpu.profile_enable(True)
+    a, la = _decode(shared, seqs, w.q, w.scale, pt=512, k_draft=k_draft)
+    torch.cuda.synchronize()
+    _, n_prefix = shared.gpu.profile_read(3)
+    shared.gpu.profile_enable(False)
+    assert n_prefix == 1, "the shared-prefix launch did not run"
+    ro, rl = oracle_decode(shared, seqs, w.q, w.scale, k_draft=k_draft)
+    assert_close(a, la, ro, rl, dtype, "shared-prefix pass")
+    nb = (len(seqs) + 1) * w.num_blocks
+    private = Pair(w, free_order=np.random.default_rng(2).permutation(nb), num_blocks=nb)
+    for s in seqs:
+        private.alloc(s)
+        k = np.concatenate([w.prefix_k, w.k_rows[s], w.new_k[s]])
+        v = np.concatenate([w.prefix_v, w.v_rows[s], w.new_v[s]])
+        private.append([s], [k.shape[0]], k, v)
+    private.gpu.profile_enable(True)
+    b, lb = _decode(private, seqs, w.q, w.scale, pt=512, k_draft=k_draft)
+    torch.cuda.synchronize()
+    assert private.gpu.profile_read(3)[1] == 0
+    private.gpu.profile_enable(False)
+    assert_close(b, lb, ro, rl, dtype, "private copies")
+
+
+def test_shared_prefix_pass_fused_append_decode():
+    """Decode step of eight forks of a 1,536-token prefix as one
+    pa_append_attend call: shared-prefix launch, then the fused append +
+    attention launch over the rest; matches the two-call path and the oracle."""
+    w = make_custom(lengths=[5, 40, 300, 17, 600, 90, 1, 250], mode="append_decode", num_q_heads=32,
+                    num_kv_heads=8, head_dim=128, dtype="bf16", seed=38, prefix_len=1536)
+    _fused_vs_separate(w)
+
+
 def _fused_vs_separate(w, prefix_fork_partial=False, pending_fork=False):
     """Run the same step as append + attend (two calls) and as one
     pa_append_attend call: pools, tables and outputs must be bitwise equal."""
