@@ -59,7 +59,7 @@ class StateError(PaError):
 class PoolModel:
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str,
                  max_seqs: int, max_blocks_per_seq: int, free_order=None,
-                 sentinel_bits: int = 0, track_data: bool = True):
+                 sentinel_bits: int = 0, track_data: bool = True, kv_scales=None):
         if num_blocks <= 0 or num_kv_heads <= 0 or head_dim <= 0:
             raise InvalidError("sizes must be positive")
         if free_order is None:
@@ -71,6 +71,12 @@ class PoolModel:
         self.hkv = num_kv_heads
         self.d = head_dim
         self.dtype = dtype
+        # 'fp8' pools: rows arrive as bf16 bits and are stored as E4M3 codes of
+        # row * (1 / scale) per kv head, the reciprocal and product in float32
+        if kv_scales is None:
+            kv_scales = (np.ones(num_kv_heads, np.float32), np.ones(num_kv_heads, np.float32))
+        self.k_scale = np.asarray(kv_scales[0], np.float32)
+        self.v_scale = np.asarray(kv_scales[1], np.float32)
         self.max_seqs = max_seqs
         self.max_blocks = max_blocks_per_seq
         self.free: deque = deque(free_order)
@@ -156,9 +162,20 @@ class PoolModel:
             self._release(old)
             tab[-1] = new
         if self.track_data:
-            layout.write_row(self.kpool, self.vpool, tab[-1], off,
-                             as_bits(k_row, self.dtype), as_bits(v_row, self.dtype), self.dtype)
+            if self.dtype == "fp8":
+                k_code, v_code = self._quantize(k_row, self.k_scale), self._quantize(v_row, self.v_scale)
+            else:
+                k_code, v_code = as_bits(k_row, self.dtype), as_bits(v_row, self.dtype)
+            layout.write_row(self.kpool, self.vpool, tab[-1], off, k_code, v_code, self.dtype)
         self.lens[seq] = t + 1
+
+    @staticmethod
+    def _quantize(row_bf16: np.ndarray, scale: np.ndarray) -> np.ndarray:
+        """E4M3 codes of one [Hkv, D] bf16 row: E4M3(x * (1 / scale[h]))."""
+        from .fp8 import encode
+        x = (as_bits(row_bf16, "bf16").astype(np.uint32) << np.uint32(16)).view(np.float32)
+        inv = (np.float32(1.0) / scale.astype(np.float32)).astype(np.float32)
+        return encode((x * inv[:, None]).astype(np.float32))
 
     def append(self, seq_ids, n_tok, k_rows=None, v_rows=None) -> None:
         """Append n_tok[i] rows to seq_ids[i]; rows are packed in call order

@@ -34,11 +34,12 @@ from .numerics import to_f64
 BLOCK = layout.BLOCK
 
 
-def gather(kpool: np.ndarray, vpool: np.ndarray, block_table, n: int, dtype: str):
+def gather(kpool: np.ndarray, vpool: np.ndarray, block_table, n: int, dtype: str, kv_scales=None):
     """Rows 0..n-1 of one sequence as float64 arrays [n, Hkv, D].
 
     ``kpool`` / ``vpool`` are the 5-d / 4-d pool arrays of ``oracle.layout``
-    (bit patterns or float arrays of the storage type).
+    (bit patterns or float arrays of the storage type).  For 'fp8' pools,
+    ``kv_scales`` = (k_scale[Hkv], v_scale[Hkv]) multiply the decoded codes.
     """
     hkv = kpool.shape[1]
     d = vpool.shape[2]
@@ -49,6 +50,9 @@ def gather(kpool: np.ndarray, vpool: np.ndarray, block_table, n: int, dtype: str
         k, v = layout.read_row(kpool, vpool, b, t % BLOCK, dtype)
         kc[t] = to_f64(k, dtype)
         vc[t] = to_f64(v, dtype)
+    if kv_scales is not None:
+        kc *= np.asarray(kv_scales[0], np.float64)[None, :, None]
+        vc *= np.asarray(kv_scales[1], np.float64)[None, :, None]
     return kc, vc
 
 
@@ -108,14 +112,14 @@ def verify(kc: np.ndarray, vc: np.ndarray, q: np.ndarray, scale: float):
 
 
 def decode_from_pool(kpool, vpool, block_table, n: int, q_bits: np.ndarray, scale: float,
-                     dtype: str):
+                     dtype: str, kv_scales=None):
     """Gather + decode for one sequence; q_bits [Hq, D] in the storage type."""
-    kc, vc = gather(kpool, vpool, block_table, n, dtype)
-    return decode(kc, vc, to_f64(q_bits, dtype), scale)
+    kc, vc = gather(kpool, vpool, block_table, n, dtype, kv_scales)
+    return decode(kc, vc, to_f64(q_bits, "bf16" if dtype == "fp8" else dtype), scale)
 
 
 def verify_from_pool(kpool, vpool, block_table, n: int, q_bits: np.ndarray, scale: float,
-                     dtype: str):
+                     dtype: str, kv_scales=None):
     """Gather + verify for one sequence; q_bits [K, Hq, D] in the storage type."""
-    kc, vc = gather(kpool, vpool, block_table, n, dtype)
-    return verify(kc, vc, to_f64(q_bits, dtype), scale)
+    kc, vc = gather(kpool, vpool, block_table, n, dtype, kv_scales)
+    return verify(kc, vc, to_f64(q_bits, "bf16" if dtype == "fp8" else dtype), scale)

@@ -1,15 +1,16 @@
 """Decode stored element bit patterns to float64 (oracle; test infrastructure only).
 
 Storage types: 'f32' (IEEE binary32), 'f16' (IEEE binary16), 'bf16' (the top
-16 bits of a binary32).  Arrays arrive either as float32/float16 numpy arrays
-or as raw unsigned bit patterns (uint32 / uint16); both decode exactly.
+16 bits of a binary32), 'fp8' (E4M3 codes, oracle/fp8.py; decoded unscaled).
+Arrays arrive either as float32/float16 numpy arrays or as raw unsigned bit
+patterns (uint32 / uint16 / uint8); all decode exactly.
 """
 from __future__ import annotations
 
 import numpy as np
 
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
-BITS_DTYPE = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+BITS_DTYPE = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}
 
 
 def as_bits(a: np.ndarray, dtype: str) -> np.ndarray:
@@ -32,4 +33,7 @@ def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
         return bits.view(np.float16).astype(np.float64)
     if dtype == "bf16":
         return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype == "fp8":
+        from .fp8 import decode
+        return decode(bits)
     raise ValueError(dtype)
