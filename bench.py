@@ -31,8 +31,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged-attn decode effective HBM GB/s (% of MI355X peak); µs/step at batch 256"
 PEAK_GBS = 8000.0  # MI355X HBM3E, AMD public specification
-FILL = {"f32": 0x7FBADBAD, "f16": 0x7E5A, "bf16": 0x7FDA}
-EB = {"f32": 4, "f16": 2, "bf16": 2}
+FILL = {"f32": 0x7FBADBAD, "f16": 0x7E5A, "bf16": 0x7FDA, "fp8": 0x7F}
+EB = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 
 
 def parse():
@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--kv-cache", default="same", choices=["same", "fp8"],
+                    help="pool element type: the workload's own, or E4M3 codes with one scale per kv head "
+                         "(bf16 workloads only; rows, queries and outputs stay bf16)")
     ap.add_argument("--separate", action="store_true",
                     help="issue the append and the attention as two calls instead of pa_append_attend")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -72,38 +75,60 @@ def step_lengths(w):
     return [int(n) for n in w.final_lengths()]
 
 
-def decode_bytes(w) -> int:
+def decode_bytes(w, kv_eb) -> int:
     """Algorithmic bytes of one attention launch: every K and V row of every KV
-    head once (a shared prefix once), Q read, O written, block-table entries used
-    and one length per sequence."""
+    head once (a shared prefix once) at kv_eb bytes per element, Q read, O
+    written, block-table entries used and one length per sequence."""
     lens = step_lengths(w)
     e = EB[w.dtype]
     rows = sum(n - w.prefix_len for n in lens) + (w.prefix_len if lens else 0)
-    kv = rows * w.num_kv_heads * w.head_dim * e * 2
+    kv = rows * w.num_kv_heads * w.head_dim * kv_eb * 2
     qo = 2 * len(lens) * w.k_draft * w.num_q_heads * w.head_dim * e
     tab = sum(math.ceil(n / 16) for n in lens) * 4 + 4 * len(lens)
     return kv + qo + tab
 
 
-def append_bytes(w) -> int:
+def append_bytes(w, kv_eb) -> int:
+    """New K and V rows read in the workload's type and written at kv_eb bytes
+    per element, plus one slot index per row."""
     if w.new_k is None or w.mode not in ("append_decode", "verify"):
         return 0
     rows = w.new_k.shape[0] * w.new_k.shape[1]
-    return 4 * rows * w.num_kv_heads * w.head_dim * EB[w.dtype] + 4 * rows
+    return 2 * rows * w.num_kv_heads * w.head_dim * (EB[w.dtype] + kv_eb) + 4 * rows
+
+
+def fp8_scales(w):
+    """One scale per kv head for E4M3 pools: the largest magnitude of that
+    head's rows (prefix, cached and new) maps to 448, the largest code."""
+    def amax(parts):
+        m = np.zeros(w.num_kv_heads)
+        for a in parts:
+            if a is None or a.size == 0:
+                continue
+            x = (np.asarray(a).view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+            x = x.reshape(-1, w.num_kv_heads, w.head_dim)
+            m = np.maximum(m, np.abs(x).max(axis=(0, 2)))
+        return np.maximum(m, 1e-6) / 448.0
+    ks = amax([w.prefix_k] + list(w.k_rows) + [w.new_k])
+    vs = amax([w.prefix_v] + list(w.v_rows) + [w.new_v])
+    return ks.astype(np.float32), vs.astype(np.float32)
 
 
 class Replica:
     """One filled pool plus the pre-marshalled arguments of a step."""
 
-    def __init__(self, w, pt, separate=False):
+    def __init__(self, w, pt, separate=False, cache_dtype=None, scales=None):
         import torch
         from paged_kv_cache_216_amd.cache import PagedKVCache
 
         self.w = w
         b = w.batch
-        self.cache = PagedKVCache(w.num_blocks, w.num_kv_heads, w.head_dim, w.dtype, b, w.max_blocks_per_seq,
-                                  free_order=w.free_order, fill_bits=FILL[w.dtype])
+        cd = cache_dtype or w.dtype
+        self.cache = PagedKVCache(w.num_blocks, w.num_kv_heads, w.head_dim, cd, b, w.max_blocks_per_seq,
+                                  free_order=w.free_order, fill_bits=FILL[cd])
         c = self.cache
+        if scales is not None:
+            c.set_kv_scales(*scales)
         if w.prefix_len:
             c.alloc(0)
             c.append([0], [w.prefix_len], to_torch(w.prefix_k, w.dtype), to_torch(w.prefix_v, w.dtype))
@@ -185,7 +210,7 @@ def describe(w) -> str:
     return d[w.name]
 
 
-def cpu_baseline(w, budget_s):
+def cpu_baseline(w, budget_s, cache_dtype, scales):
     """The float64 oracle, single-threaded, on the first sequences of the same
     workload until `budget_s` seconds of work; reported in the metric's unit."""
     from threadpoolctl import threadpool_limits
@@ -197,8 +222,8 @@ def cpu_baseline(w, budget_s):
     done_bytes, elapsed, nseq, ntok = 0, 0.0, 0, 0
     with threadpool_limits(limits=1):
         for s in range(w.batch):
-            m = PoolModel(w.num_blocks, w.num_kv_heads, w.head_dim, w.dtype, 1, w.max_blocks_per_seq,
-                          free_order=w.free_order)
+            m = PoolModel(w.num_blocks, w.num_kv_heads, w.head_dim, cache_dtype, 1, w.max_blocks_per_seq,
+                          free_order=w.free_order, kv_scales=scales)
             m.alloc(0)
             parts_k, parts_v = [], []
             if w.prefix_len:
@@ -213,12 +238,13 @@ def cpu_baseline(w, budget_s):
             t0 = time.perf_counter()
             m.append([0], [k.shape[0]], k, v)
             if w.k_draft == 1:
-                A.decode_from_pool(m.kpool, m.vpool, m.table(0), m.length(0), w.q[s, 0], w.scale, w.dtype)
+                A.decode_from_pool(m.kpool, m.vpool, m.table(0), m.length(0), w.q[s, 0], w.scale, cache_dtype,
+                                   scales)
             else:
-                A.verify_from_pool(m.kpool, m.vpool, m.table(0), m.length(0), w.q[s], w.scale, w.dtype)
+                A.verify_from_pool(m.kpool, m.vpool, m.table(0), m.length(0), w.q[s], w.scale, cache_dtype, scales)
             elapsed += time.perf_counter() - t0
             n = lens[s]
-            done_bytes += (n * w.num_kv_heads * w.head_dim * EB[w.dtype] * 2
+            done_bytes += (n * w.num_kv_heads * w.head_dim * EB[cache_dtype] * 2
                            + 2 * w.k_draft * w.num_q_heads * w.head_dim * EB[w.dtype] + math.ceil(n / 16) * 4 + 4)
             nseq += 1
             ntok += n
@@ -277,8 +303,14 @@ def main():
     torch.cuda.set_device(0)
     w = make_workload(args.workload)
     pt = args.partition_tokens if args.partition_tokens else (w.partition_tokens or 0)
-    print(f"bench: building {args.replicas} replica pools for '{w.name}'", file=sys.stderr, flush=True)
-    reps = [Replica(w, pt, args.separate) for _ in range(args.replicas)]
+    cd, scales, wkey = w.dtype, None, w.name
+    if args.kv_cache == "fp8":
+        if w.dtype != "bf16":
+            print("bench.py: --kv-cache fp8 takes bf16 workloads", flush=True)
+            sys.exit(2)
+        cd, scales, wkey = "fp8", fp8_scales(w), w.name + "_fp8"
+    print(f"bench: building {args.replicas} replica pools for '{wkey}'", file=sys.stderr, flush=True)
+    reps = [Replica(w, pt, args.separate, cd, scales) for _ in range(args.replicas)]
     stream = torch.cuda.current_stream()
     sh = ctypes.c_void_p(stream.cuda_stream)
     if args.copy_calibration_mib:
@@ -339,11 +371,12 @@ def main():
         st = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
         pct = {"p50": round(float(np.percentile(st, 50)), 2), "p90": round(float(np.percentile(st, 90)), 2),
                "p99": round(float(np.percentile(st, 99)), 2), "mean": round(float(st.mean()), 2)}
-    dec_b = decode_bytes(w)
-    app_b = append_bytes(w)
+    dec_b = decode_bytes(w, EB[cd])
+    app_b = append_bytes(w, EB[cd])
     step_b = dec_b + app_b
     value = step_b / (ms_step * 1e-3) / 1e9
-    fused = bool(reps[0].t_new) and not args.separate
+    # 8-bit pools take the append and the attention as two launches
+    fused = bool(reps[0].t_new) and not args.separate and cd != "fp8"
     roof = None
     if kern[0][1]:
         attn_ms = kern[0][0] / kern[0][1]
@@ -352,7 +385,7 @@ def main():
         kname = "attn_append_kernel" if fused else "attn_kernel"
         achieved = launch_b / (attn_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_GBS, 4), "traffic": measured_traffic(w.name, kname),
+                "frac": round(achieved / PEAK_GBS, 4), "traffic": measured_traffic(wkey, kname),
                 "kernel": kname, "avg_us": round(attn_ms * 1e3, 2), "bytes_per_launch": launch_b,
                 "timing": "HIP events around each launch on its stream, over a second pass of the timed steps"}
     line = {
@@ -360,7 +393,9 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "us_per_step": round(ms_step * 1e3, 2),
         "pct_of_peak": round(100 * value / PEAK_GBS, 2), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": f"{w.name}: {describe(w)}", "batch": w.batch, "seed": w.seed,
+        "config": {"workload": f"{wkey}: {describe(w)}" + (
+                       "; key/value pools in E4M3 with one scale per kv head (amax / 448)" if cd == "fp8" else ""),
+                   "kv_cache": cd, "batch": w.batch, "seed": w.seed,
                    "replicas": args.replicas, "partition_tokens": pt or "library choice (512 when split)",
                    "bytes_per_step": step_b, "decode_bytes": dec_b, "append_bytes": app_b,
                    "cached_tokens": int(sum(step_lengths(w)))},
@@ -371,12 +406,14 @@ def main():
         "step_us_percentiles": pct,
         "host_wall_ms_per_step": round(1e3 * wall / args.steps, 4),
         "host_enqueue_us_per_step": round(1e6 * t_enq / args.steps, 2),
-        "step_calls": "pa_append_attend" if fused else ("pa_append_kv + attention" if reps[0].t_new else "attention"),
+        "step_calls": ("pa_append_attend" if fused else
+                       "pa_append_attend (append and attention launches)" if reps[0].t_new and not args.separate else
+                       "pa_append_kv + attention" if reps[0].t_new else "attention"),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, cd, scales)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -31,7 +31,8 @@
  *   - A pool is not thread-safe.
  *
  * Physical layout (caller allocates; bit patterns are the contract):
- *   element size e = 4 (PA_F32) or 2 (PA_F16, PA_BF16); X = 16 / e
+ *   element size e = 4 (PA_F32), 2 (PA_F16, PA_BF16) or 1 (PA_FP8_E4M3);
+ *   X = 16 / e
  *   K pool: [num_blocks][num_kv_heads][head_dim / X][16][X]
  *   V pool: [num_blocks][num_kv_heads][head_dim][16]
  *   so one (block, head) K or V page is 16 * head_dim * e contiguous bytes,
@@ -63,7 +64,17 @@ typedef enum {
   PA_ERR_STATE = -4    /* call not possible in this pool's state (e.g. host-only) */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+/* PA_FP8_E4M3: the pools hold one-byte E4M3 codes (1 sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits; no infinities; largest finite value 448),
+ * one scale per (K or V, kv head) (pa_set_kv_scales).  Rows appended, queries
+ * and outputs are bf16.  The stored code of an element x of key/value head h
+ * is E4M3(x * r) with r = 1.0f / scale[h] in float32: the product is rounded
+ * to float32, clamped to [-448, 448] and rounded to the nearest code, ties to
+ * the even code; the attention uses decode(code) * scale[h], in fp32.  An
+ * 8-bit cache halves the bytes a decode step reads while the softmax stays at
+ * full precision (ranksignal.fr post 218, "Quantifier").  The 8-bit pools take
+ * neither the single-launch append + attention nor the shared-prefix pass. */
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
 
 /* Create a pool over caller-owned device memory.
  *   num_blocks      physical blocks in k_pool / v_pool (> 0)
@@ -99,6 +110,12 @@ int pa_destroy_pool(pa_pool* pool);
  * fork.  With parent_seq < 0, shared_tokens must be 0.  Host-side only; the
  * device table rows are written by the next device call. */
 int pa_alloc_blocks(pa_pool* pool, int seq_id, int parent_seq, int shared_tokens);
+
+/* Scales of a PA_FP8_E4M3 pool, one per kv head: host float arrays
+ * [num_kv_heads], finite and > 0 (default 1.0).  Codes already stored are
+ * not rewritten: set the scales before the first append.  Synchronous.
+ * PA_ERR_STATE for pools of other dtypes. */
+int pa_set_kv_scales(pa_pool* pool, const float* k_scale, const float* v_scale);
 
 /* Append n_tok[i] new K/V rows to sequence seq_ids[i], i = 0..n_seq-1.
  *   seq_ids, n_tok  host int32 [n_seq]; sequences live and distinct;

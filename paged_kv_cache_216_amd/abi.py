@@ -12,7 +12,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpa.so")
 
 PA_OK, PA_ERR_INVALID, PA_ERR_NOMEM, PA_ERR_HIP, PA_ERR_STATE = 0, -1, -2, -3, -4
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 
 c_int, c_float, c_size_t, c_void_p = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 c_i32p = ctypes.POINTER(ctypes.c_int32)
@@ -27,6 +27,7 @@ SIGNATURES = {
                                c_void_p, c_void_p, c_void_p, c_int, c_int, c_i32p]),
     "pa_destroy_pool": (c_int, [c_void_p]),
     "pa_alloc_blocks": (c_int, [c_void_p, c_int, c_int, c_int]),
+    "pa_set_kv_scales": (c_int, [c_void_p, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]),
     "pa_append_kv": (c_int, [c_void_p, c_i32p, c_int, c_i32p, c_void_p, c_void_p, c_void_p]),
     "pa_decode": (c_int, [c_void_p, c_i32p, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p, c_int,
                           c_void_p, c_size_t, c_void_p]),

@@ -13,9 +13,11 @@ import torch
 
 from . import abi
 
-TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
-PA_DTYPES = {"f32": abi.PA_F32, "f16": abi.PA_F16, "bf16": abi.PA_BF16}
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+# "fp8": pools of E4M3 codes (uint8 tensors); rows, queries and outputs are bf16
+TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.bfloat16}
+POOL_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.uint8}
+PA_DTYPES = {"f32": abi.PA_F32, "f16": abi.PA_F16, "bf16": abi.PA_BF16, "fp8": abi.PA_FP8_E4M3}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 BLOCK = 16
 
 
@@ -58,11 +60,11 @@ class PagedKVCache:
             self.k_pool = self.v_pool = self.block_table = self.seq_len = None
         else:
             self.k_pool = torch.empty(k_pool_shape(num_blocks, num_kv_heads, head_dim, dtype),
-                                      dtype=self.tdtype, device=device)
+                                      dtype=POOL_DTYPES[dtype], device=device)
             self.v_pool = torch.empty(v_pool_shape(num_blocks, num_kv_heads, head_dim, dtype),
-                                      dtype=self.tdtype, device=device)
+                                      dtype=POOL_DTYPES[dtype], device=device)
             if fill_bits is not None:
-                ibits = torch.int32 if ELEM_BYTES[dtype] == 4 else torch.int16
+                ibits = {4: torch.int32, 2: torch.int16, 1: torch.int8}[ELEM_BYTES[dtype]]
                 val = int(fill_bits)
                 nbits = 8 * ELEM_BYTES[dtype]
                 if val >= 1 << (nbits - 1):
@@ -93,6 +95,12 @@ class PagedKVCache:
             self.close()
         except Exception:
             pass
+
+    def set_kv_scales(self, k_scale: Sequence[float], v_scale: Sequence[float]) -> None:
+        """Per-kv-head scales of an "fp8" pool (before the first append)."""
+        fa = ctypes.c_float * self.hkv
+        abi.check(self.lib.pa_set_kv_scales(self.handle, fa(*[float(x) for x in k_scale]),
+                                            fa(*[float(x) for x in v_scale])))
 
     # ---- block bookkeeping -------------------------------------------------
     def alloc(self, seq: int, parent: int = -1, shared_tokens: int = 0) -> None:

@@ -59,10 +59,20 @@ __host__ __device__ inline AppendGrid append_grid(const AppendParams& p, int nth
 // updates, copies of the filled slots of shared blocks (rows [0, off) only, so
 // they never overlap the slots this call writes), and one 16-byte chunk of a
 // new row per thread.
-template <int E>  // element bytes: 2 or 4
+// E4M3 code of a float: clamp to the largest finite magnitude (448), then
+// round to nearest, ties to even (the conversion instruction's rounding).
+__device__ inline uint32_t fp8_pack4(float a, float b, float c, float d) {
+  auto cl = [](float x) { return fminf(fmaxf(x, -448.f), 448.f); };
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
+}
+
+__device__ inline float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }
+
+template <int E>  // element bytes of the pool: 1 (E4M3, bf16 rows in), 2 or 4
 __device__ inline void append_work(const AppendParams& p, const int32_t* meta, int b, int nthreads) {
-  using Elem = std::conditional_t<E == 2, uint16_t, uint32_t>;
-  constexpr int X = 16 / E;  // elements per 16-byte chunk
+  using Elem = std::conditional_t<E == 1, uint8_t, std::conditional_t<E == 2, uint16_t, uint32_t>>;
+  constexpr int X = 16 / E;  // elements per 16-byte chunk of the pool
   const AppendGrid g = append_grid(p, nthreads);
   const int D = p.head_dim;
   const int nchunk = D / X;                               // chunks per (head, slot)
@@ -105,6 +115,45 @@ __device__ inline void append_work(const AppendParams& p, const int32_t* meta, i
   }
   b -= g.cow_blocks;
 
+  if constexpr (E == 1) {
+    // rows: one thread per 16 bytes (8 bf16) of one row, quantized to 8 codes
+    const int per_head = D / 8;
+    const int chunks_per_row = p.hkv * per_head;
+    const long long w = static_cast<long long>(b) * nthreads + tid;
+    if (w >= static_cast<long long>(p.n_rows) * chunks_per_row) return;
+    const int row = static_cast<int>(w / chunks_per_row);
+    const int c = static_cast<int>(w % chunks_per_row);
+    const int h = c / per_head;
+    const int cc = c % per_head;  // dims 8 cc .. 8 cc + 7
+    const int slot = meta[p.slots + row];
+    const u32x4 kv = reinterpret_cast<const u32x4*>(p.k_new)[static_cast<size_t>(row) * chunks_per_row + c];
+    const u32x4 vv = reinterpret_cast<const u32x4*>(p.v_new)[static_cast<size_t>(row) * chunks_per_row + c];
+    const float ki = p.kv_scale[2 * p.hkv + h], vi = p.kv_scale[3 * p.hkv + h];
+    float kf[8], vf[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kf[2 * i] = bf16_bits_to_float(kv[i] & 0xFFFFu) * ki;
+      kf[2 * i + 1] = bf16_bits_to_float(kv[i] >> 16) * ki;
+      vf[2 * i] = bf16_bits_to_float(vv[i] & 0xFFFFu) * vi;
+      vf[2 * i + 1] = bf16_bits_to_float(vv[i] >> 16) * vi;
+    }
+    const int phys = slot / kBlk;
+    const int t = slot % kBlk;
+    // K: the 8 codes are half of 16-byte chunk cc / 2 of slot t
+    uint8_t* kdst = static_cast<uint8_t*>(p.k_pool) +
+                    (((static_cast<size_t>(phys) * p.hkv + h) * nchunk + cc / 2) * kBlk + t) * 16 + 8 * (cc & 1);
+    *reinterpret_cast<u32x2*>(kdst) = u32x2{fp8_pack4(kf[0], kf[1], kf[2], kf[3]), fp8_pack4(kf[4], kf[5], kf[6], kf[7])};
+    // V: one code per dim, kBlk bytes apart
+    const uint32_t v0 = fp8_pack4(vf[0], vf[1], vf[2], vf[3]), v1 = fp8_pack4(vf[4], vf[5], vf[6], vf[7]);
+    uint8_t* vdst = static_cast<uint8_t*>(p.v_pool) + (static_cast<size_t>(phys) * p.hkv + h) * page +
+                    static_cast<size_t>(8 * cc) * kBlk + t;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      vdst[i * kBlk] = static_cast<uint8_t>(v0 >> (8 * i));
+      vdst[(4 + i) * kBlk] = static_cast<uint8_t>(v1 >> (8 * i));
+    }
+    return;
+  }
   // rows: one thread per 16-byte chunk of one row (all heads)
   const int chunks_per_row = p.hkv * nchunk;
   const long long w = static_cast<long long>(b) * nthreads + tid;
@@ -352,21 +401,65 @@ __device__ inline void merge_last(const AttnParams& p, const Unit& u, int kvh) {
 }
 
 // 16-bit element types: bf16 or f16
-template <typename T, int D, int NT, bool NTL, bool FUSED, bool PREFIX = false>
+// E4M3 codes to bf16 (exact: every E4M3 value is a bf16 value).  One
+// conversion per byte: hipcc mis-tracks the second result of the two-code
+// conversion (v_cvt_pk_f32_fp8) once its bits are reused, so it is not used.
+__device__ inline __bf16 fp8_to_bf16(uint32_t w, int byte) {
+  float f = 0.f;
+  switch (byte) {  // the byte select must be an immediate
+    case 0: f = __builtin_amdgcn_cvt_f32_fp8(w, 0); break;
+    case 1: f = __builtin_amdgcn_cvt_f32_fp8(w, 1); break;
+    case 2: f = __builtin_amdgcn_cvt_f32_fp8(w, 2); break;
+    default: f = __builtin_amdgcn_cvt_f32_fp8(w, 3); break;
+  }
+  return static_cast<__bf16>(f);
+}
+
+__device__ inline bf16x8 fp8x8_to_bf16(u32x2 w) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = fp8_to_bf16(w[0], i);
+    r[4 + i] = fp8_to_bf16(w[1], i);
+  }
+  return r;
+}
+
+__device__ inline u32x2 fp8x4_to_bf16(uint32_t w) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = fp8_to_bf16(w, i);
+  return __builtin_bit_cast(u32x2, r);
+}
+
+template <bool NTL>
+__device__ inline uint32_t page_load4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, NTL ? 2 : 0));
+}
+
+// Q8: the pool holds E4M3 codes (T is bf16): K and V are loaded at one byte
+// per element, converted exactly to bf16 in registers, and the per-head
+// scales fold into the score scale (K) and the output (V).
+template <typename T, int D, int NT, bool NTL, bool FUSED, bool PREFIX = false, bool Q8 = false>
 __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) {
+  static_assert(!(Q8 && (FUSED || PREFIX)), "E4M3 pools take the plain path");
   using Op = typename MfmaOp<T>::type;
   constexpr int KS = D / 32;  // QK k-steps per block
   constexpr int DC = D / 16;  // output dim chunks
-  constexpr int kPageBytes = D * kBlk * static_cast<int>(sizeof(T));
+  constexpr int kPageBytes = D * kBlk * (Q8 ? 1 : static_cast<int>(sizeof(T)));
+  const float sl2 = Q8 ? p.scale_log2 * p.kv_scale[kvh] : p.scale_log2;  // score scale, log2 domain
+  const float vsc = Q8 ? p.kv_scale[p.hkv + kvh] : 1.f;
   const int lane = threadIdx.x & 63;  // one wave; the shared-prefix pass runs several per workgroup
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int rows = p.rows;
   const int G = p.group;
 
-  const T* kpool = static_cast<const T*>(p.k_pool);
-  const T* vpool = static_cast<const T*>(p.v_pool);
-  const size_t page = static_cast<size_t>(D) * kBlk;
+  using PoolElem = std::conditional_t<Q8, uint8_t, T>;
+  const PoolElem* kpool = static_cast<const PoolElem*>(p.k_pool);
+  const PoolElem* vpool = static_cast<const PoolElem*>(p.v_pool);
+  const size_t page = static_cast<size_t>(D) * kBlk;  // elements (bytes for E4M3) per (block, head)
   const int32_t* bt = p.block_table + static_cast<size_t>(u.seq) * p.max_blocks;
   const int jb0 = u.tok_begin / kBlk;
 
@@ -438,6 +531,14 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
     Op k0[KS], k1[KS];
     u32x2 v0[DC], v1[DC];
   };
+  // E4M3 pools: a pair as loaded, one byte per element (half the registers of
+  // a 16-bit pair, so two pairs stay in flight for the bytes of one), turned
+  // into bf16 operands just before they are used
+  struct Frag8 {
+    u32x2 k0[KS], k1[KS];
+    uint32_t v0[DC], v1[DC];
+  };
+  using LFrag = std::conditional_t<Q8, Frag8, Frag>;
   // Scores, online softmax and PV for the 32 tokens starting at pos0; tokens at
   // or beyond `end` are masked (and their V zeroed: such slots may hold anything).
   auto process = [&](Frag& f, int pos0, int end) {
@@ -456,8 +557,8 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       float x[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[e] = s0[e] * p.scale_log2;
-        x[4 + e] = s1[e] * p.scale_log2;
+        x[e] = s0[e] * sl2;
+        x[4 + e] = s1[e] * sl2;
       }
       if (need_mask) {
 #pragma unroll
@@ -529,7 +630,7 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
     // resource with no valid bytes, so its loads return zeros and touch no
     // memory.  Uniform control flow lets the compiler wait only for the pair
     // being computed.
-    auto load = [&](Frag& f, int pj) {
+    auto load = [&](LFrag& f, int pj) {
       const int j = 2 * pj;
       const int bytes0 = j < cnt ? kPageBytes : 0;
       const int bytes1 = j + 1 < cnt ? kPageBytes : 0;
@@ -539,6 +640,22 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       const size_t off1 = (static_cast<size_t>(phys1) * p.hkv + kvh) * page;
       const auto rk0 = page_rsrc(kpool + off0, bytes0), rv0 = page_rsrc(vpool + off0, bytes0);
       const auto rk1 = page_rsrc(kpool + off1, bytes1), rv1 = page_rsrc(vpool + off1, bytes1);
+      if constexpr (Q8) {
+        // K: 8 codes = dims 32 s + 8 grp .. + 7 of token col, half of a 16-byte chunk
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const int o = ((2 * s + (grp >> 1)) * kBlk + col) * 16 + 8 * (grp & 1);
+          f.k0[s] = page_load8<NTL>(rk0, o);
+          f.k1[s] = page_load8<NTL>(rk1, o);
+        }
+        // V: 4 codes = tokens 4 grp .. + 3 of dim 16 c + col
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          const int o = (16 * c + col) * kBlk + 4 * grp;
+          f.v0[c] = page_load4<NTL>(rv0, o);
+          f.v1[c] = page_load4<NTL>(rv1, o);
+        }
+      } else {
 #pragma unroll
       for (int s = 0; s < KS; ++s)
         f.k0[s] = __builtin_bit_cast(Op, page_load16<NTL>(rk0, ((4 * s + grp) * kBlk + col) * 16));
@@ -549,6 +666,7 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       for (int c = 0; c < DC; ++c) f.v0[c] = page_load8<NTL>(rv0, ((16 * c + col) * kBlk + 4 * grp) * 2);
 #pragma unroll
       for (int c = 0; c < DC; ++c) f.v1[c] = page_load8<NTL>(rv1, ((16 * c + col) * kBlk + 4 * grp) * 2);
+      }
     };
     const int base_pos = (jb0 + cb) * kBlk;
     // One pair in flight per wave is enough to saturate HBM with two waves
@@ -556,7 +674,39 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
     // dependent access (measured on MI355X: 3-6 % faster than keeping two
     // pairs in flight).  Multi-tile (verify) waves do more math per pair and
     // keep the second pair in flight.
-    if constexpr (NT >= 2 && D * NT < 512) {
+    if constexpr (Q8) {
+      auto run = [&](Frag8& r, int pos0) {
+        Frag f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          f.k0[s] = __builtin_bit_cast(Op, fp8x8_to_bf16(r.k0[s]));
+          f.k1[s] = __builtin_bit_cast(Op, fp8x8_to_bf16(r.k1[s]));
+        }
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          f.v0[c] = fp8x4_to_bf16(r.v0[c]);
+          f.v1[c] = fp8x4_to_bf16(r.v1[c]);
+        }
+        process(f, pos0, pool_end);
+      };
+      if constexpr (D * NT <= 256) {
+        Frag8 ra, rb;
+        load(ra, 0);
+        for (int pj = 0; pj < npairs; pj += 2) {
+          load(rb, pj + 1);
+          run(ra, base_pos + 2 * pj * kBlk);
+          if (pj + 1 >= npairs) break;
+          load(ra, pj + 2);
+          run(rb, base_pos + (2 * pj + 2) * kBlk);
+        }
+      } else {  // wide tiles: the registers hold one pair in flight
+        for (int pj = 0; pj < npairs; ++pj) {
+          Frag8 r;
+          load(r, pj);
+          run(r, base_pos + 2 * pj * kBlk);
+        }
+      }
+    } else if constexpr (NT >= 2 && D * NT < 512) {
       Frag fa, fb;
       load(fa, 0);
       for (int pj = 0; pj < npairs; pj += 2) {
@@ -692,7 +842,7 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
     if (u.slot_base < 0) {
       float inv[4];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) inv[jj] = 1.f / shfl_f(l, 4 * grp + jj);
+      for (int jj = 0; jj < 4; ++jj) inv[jj] = vsc / shfl_f(l, 4 * grp + jj);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int r = nt * 16 + 4 * grp + jj;
@@ -723,9 +873,9 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
 #pragma unroll
           for (int c = 0; c < DC; ++c) {
             if constexpr (NT == 1)
-              store_device(ap + 16 * c + col, acc[nt][c][jj]);
+              store_device(ap + 16 * c + col, acc[nt][c][jj] * vsc);
             else
-              ap[16 * c + col] = acc[nt][c][jj];
+              ap[16 * c + col] = acc[nt][c][jj] * vsc;
           }
         }
       }
@@ -906,7 +1056,7 @@ __device__ inline void attn_body32(const AttnParams& p, const Unit& u, int kvh) 
 }
 
 // One workgroup (one wave) per (work unit, key/value head).
-template <typename T, int D, int NT, bool NTL, bool FUSED>
+template <typename T, int D, int NT, bool NTL, bool FUSED, bool Q8 = false>
 __device__ inline void attn_unit(const AttnParams& p, const int32_t* meta) {
   const int unit = blockIdx.x / p.hkv;
   const int kvh = blockIdx.x - unit * p.hkv;
@@ -931,12 +1081,12 @@ __device__ inline void attn_unit(const AttnParams& p, const int32_t* meta) {
   if constexpr (std::is_same_v<T, float>)
     attn_body32<D, NT>(p, u, kvh);
   else
-    attn_body16<T, D, NT, NTL, FUSED>(p, u, kvh);
+    attn_body16<T, D, NT, NTL, FUSED, false, Q8>(p, u, kvh);
 }
 
-template <typename T, int D, int NT, bool NTL>
+template <typename T, int D, int NT, bool NTL, bool Q8 = false>
 __global__ __launch_bounds__(64) void attn_kernel(AttnParams p) {
-  attn_unit<T, D, NT, NTL, false>(p, nullptr);
+  attn_unit<T, D, NT, NTL, false, Q8>(p, nullptr);
 }
 
 // Attention and append in one launch: workgroups past the attention grid do
@@ -1066,9 +1216,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
   }
 }
 
-template <typename T, int D, int NT, bool NTL>
+template <typename T, int D, int NT, bool NTL, bool Q8>
 void launch_attn_nt(const AttnParams& p, const InlineMeta& m, hipStream_t stream) {
-  if constexpr (!std::is_same_v<T, float>) {
+  if constexpr (!std::is_same_v<T, float> && !Q8) {
     if (p.t_new > 0) {
       const dim3 grid(static_cast<unsigned>(p.n_units) * p.hkv + p.app_blocks);
       hipLaunchKernelGGL((attn_append_kernel<T, D, NT, NTL>), grid, dim3(64), 0, stream, p, m);
@@ -1076,31 +1226,34 @@ void launch_attn_nt(const AttnParams& p, const InlineMeta& m, hipStream_t stream
     }
   }
   const dim3 grid(static_cast<unsigned>(p.n_units) * p.hkv);
-  hipLaunchKernelGGL((attn_kernel<T, D, NT, NTL>), grid, dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((attn_kernel<T, D, NT, NTL, Q8>), grid, dim3(64), 0, stream, p);
 }
 
-template <typename T, int D, bool NTL>
+template <typename T, int D, bool NTL, bool Q8>
 hipError_t launch_attn_d(const AttnParams& p, const InlineMeta& m, hipStream_t stream) {
-  if (std::is_same_v<T, float> && p.t_new > 0) return hipErrorInvalidValue;  // no fused fp32 path
+  // no fused fp32 or E4M3 path
+  if ((std::is_same_v<T, float> || Q8) && p.t_new > 0) return hipErrorInvalidValue;
   const int nt = (p.rows + 15) / 16;
   if (nt <= 1)
-    launch_attn_nt<T, D, 1, NTL>(p, m, stream);
+    launch_attn_nt<T, D, 1, NTL, Q8>(p, m, stream);
   else if (nt <= 2)
-    launch_attn_nt<T, D, 2, NTL>(p, m, stream);
+    launch_attn_nt<T, D, 2, NTL, Q8>(p, m, stream);
   else if constexpr (D <= 128)
-    launch_attn_nt<T, D, 4, NTL>(p, m, stream);
+    launch_attn_nt<T, D, 4, NTL, Q8>(p, m, stream);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool Q8 = false>
 hipError_t launch_attn_t(const AttnParams& p, const InlineMeta& m, hipStream_t stream) {
   const bool ntl = p.stream_kv != 0 && !std::is_same_v<T, float>;
   switch (p.head_dim) {
-    case 64: return ntl ? launch_attn_d<T, 64, true>(p, m, stream) : launch_attn_d<T, 64, false>(p, m, stream);
-    case 128: return ntl ? launch_attn_d<T, 128, true>(p, m, stream) : launch_attn_d<T, 128, false>(p, m, stream);
-    case 256: return ntl ? launch_attn_d<T, 256, true>(p, m, stream) : launch_attn_d<T, 256, false>(p, m, stream);
+    case 64: return ntl ? launch_attn_d<T, 64, true, Q8>(p, m, stream) : launch_attn_d<T, 64, false, Q8>(p, m, stream);
+    case 128:
+      return ntl ? launch_attn_d<T, 128, true, Q8>(p, m, stream) : launch_attn_d<T, 128, false, Q8>(p, m, stream);
+    case 256:
+      return ntl ? launch_attn_d<T, 256, true, Q8>(p, m, stream) : launch_attn_d<T, 256, false, Q8>(p, m, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1154,7 +1307,10 @@ hipError_t launch_append(const AppendParams& p, const InlineMeta* meta, hipStrea
   const long long blocks = static_cast<long long>(g.upd_blocks) + g.cow_blocks + g.row_blocks;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (p.elem_bytes == 2)
+  if (p.q8)
+    hipLaunchKernelGGL((append_kernel<1>), dim3(static_cast<unsigned>(blocks)), dim3(kAppendThreads), 0, stream, p,
+                       *meta);
+  else if (p.elem_bytes == 2)
     hipLaunchKernelGGL((append_kernel<2>), dim3(static_cast<unsigned>(blocks)), dim3(kAppendThreads), 0, stream, p,
                        *meta);
   else
@@ -1179,7 +1335,8 @@ hipError_t launch_merge_t(const AttnParams& p, hipStream_t stream) {
 hipError_t launch_merge(DType dt, const AttnParams& p, hipStream_t stream) {
   if (p.n_merges == 0) return hipSuccess;
   switch (dt) {
-    case kBF16: return launch_merge_t<__bf16>(p, stream);
+    case kBF16:
+    case kFP8: return launch_merge_t<__bf16>(p, stream);
     case kF16: return launch_merge_t<_Float16>(p, stream);
     case kF32: return launch_merge_t<float>(p, stream);
   }
@@ -1190,6 +1347,7 @@ hipError_t launch_attention(DType dt, const AttnParams& p, const InlineMeta* met
   if (p.n_units == 0 && (p.t_new == 0 || p.app_blocks == 0)) return hipSuccess;
   switch (dt) {
     case kBF16: return launch_attn_t<__bf16>(p, *meta, stream);
+    case kFP8: return launch_attn_t<__bf16, true>(p, *meta, stream);
     case kF16: return launch_attn_t<_Float16>(p, *meta, stream);
     case kF32: return launch_attn_t<float>(p, *meta, stream);
   }

@@ -8,7 +8,9 @@
 
 namespace pa {
 
-enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+// kFP8: pools hold E4M3 codes (one byte per element); the rows appended, the
+// queries and the outputs are bf16, and each (K or V, kv head) has a scale.
+enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2, kFP8 = 3 };
 
 // Per-call int32 metadata travels inside the launch's kernel arguments when it
 // fits (no copy, no host-memory reads from the GPU); larger metadata is read by
@@ -34,7 +36,9 @@ struct AppendParams {
   const int32_t* ext;  // metadata in pinned host memory, or nullptr: inline
   int tab, lens, cows, slots;
   int n_tab, n_len, n_cow, n_rows;
-  int hkv, head_dim, elem_bytes;
+  int hkv, head_dim, elem_bytes;  // elem_bytes: of the rows appended (2 for E4M3 pools)
+  int q8;                         // 1: E4M3 pool, rows are quantized on the way in
+  const float* kv_scale;          // E4M3: [4][hkv] k_scale, v_scale, 1/k_scale, 1/v_scale
 };
 
 // Work unit of the attention kernel, one per (sequence, partition); the
@@ -122,6 +126,7 @@ struct AttnParams {
   // every split sequence has at most kInlineMergeParts partitions and rows <= 16.
   unsigned* merge_ctr;
   int inline_merge;
+  const float* kv_scale;  // E4M3 pools: [4][hkv] k_scale, v_scale, 1/k_scale, 1/v_scale
   // shared-prefix pass (launch_prefix)
   const PrefixUnit* pre_units;
   const PrefixMember* pre_members;

@@ -15,6 +15,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <new>
 #include <string>
@@ -70,6 +71,9 @@ struct pa_pool {
   // cached attention plan in device memory: WorkUnits then MergeUnits
   void* dplan = nullptr;
   size_t dplan_cap = 0;  // bytes
+  // E4M3 pools: [4][hkv] k_scale, v_scale, 1/k_scale, 1/v_scale (device; host copy)
+  float* kv_scale = nullptr;
+  std::vector<float> kv_scale_host;
   // partition counters of the in-launch merge, zero between launches
   unsigned* merge_ctr = nullptr;
   size_t merge_ctr_cap = 0;  // counters
@@ -172,7 +176,9 @@ pa::AppendParams base_append(pa_pool* p) {
   ap.seq_len = p->seq_len;
   ap.hkv = p->hkv;
   ap.head_dim = p->head_dim;
-  ap.elem_bytes = p->esize;
+  ap.elem_bytes = p->dtype == PA_FP8_E4M3 ? 2 : p->esize;  // rows appended to E4M3 pools are bf16
+  ap.q8 = p->dtype == PA_FP8_E4M3 ? 1 : 0;
+  ap.kv_scale = p->kv_scale;
   return ap;
 }
 
@@ -305,7 +311,7 @@ void find_prefix_groups(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, i
   p->pre_parts.assign(n_seq, 0);
   auto& pairs = p->pre_scratch;
   pairs.clear();
-  if (pt <= 0 || p->dtype == PA_F32 || n_seq < kPrefixMinGroup) return;
+  if (pt <= 0 || (p->dtype != PA_F16 && p->dtype != PA_BF16) || n_seq < kPrefixMinGroup) return;
   for (int i = 0; i < n_seq; ++i) {
     const std::vector<int32_t>& tab = p->bp.table(seq_ids[i]);
     if (p->lens[i] - k_draft >= pt && !tab.empty() && p->bp.refcount(tab[0]) > 1) pairs.push_back({tab[0], i});
@@ -478,7 +484,7 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
     // attention reads the table while the launch's append work writes it, which
     // is safe only for the blocks this append opens (their only valid rows are
     // the new ones, which the attention takes from k_new / v_new).
-    fused = p->cows.empty() && !table_pending && p->dtype != PA_F32;
+    fused = p->cows.empty() && !table_pending && (p->dtype == PA_F16 || p->dtype == PA_BF16);
     if (!fused) {
       p->bp.take_dirty(&p->dirty);
       rc = launch_append_call(p, app->k_new, app->v_new, stream);
@@ -566,6 +572,7 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   // Short splits (few partitions, one row tile) are merged inside the
   // attention launch by the last partition to finish; others by merge_kernel.
   ak.merge_ctr = p->merge_ctr;
+  ak.kv_scale = p->kv_scale;
   ak.inline_merge = (p->dtype != PA_F32 && rows <= 16 && p->plan_max_parts <= pa::kInlineMergeParts &&
                      ws_bytes < (size_t{1} << 31)) ? 1 : 0;
   Stage* st = nullptr;
@@ -639,7 +646,8 @@ int pa_create_pool(pa_pool** out, int num_blocks, int block_size, int num_kv_hea
   if (num_kv_heads <= 0) return set_err(PA_ERR_INVALID, "num_kv_heads must be positive");
   if (head_dim != 64 && head_dim != 128 && head_dim != 256)
     return set_err(PA_ERR_INVALID, "head_dim must be 64, 128 or 256");
-  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16) return set_err(PA_ERR_INVALID, "unknown dtype");
+  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16 && dtype != PA_FP8_E4M3)
+    return set_err(PA_ERR_INVALID, "unknown dtype");
   const int ndev = (k_pool != nullptr) + (v_pool != nullptr) + (block_table_dev != nullptr) + (seq_len_dev != nullptr);
   if (ndev != 0 && ndev != 4)
     return set_err(PA_ERR_INVALID, "give all four device pointers, or none for a host-only pool");
@@ -657,7 +665,7 @@ int pa_create_pool(pa_pool** out, int num_blocks, int block_size, int num_kv_hea
   p->hkv = num_kv_heads;
   p->head_dim = head_dim;
   p->dtype = dtype;
-  p->esize = dtype == PA_F32 ? 4 : 2;
+  p->esize = dtype == PA_F32 ? 4 : (dtype == PA_FP8_E4M3 ? 1 : 2);
   p->k_pool = k_pool;
   p->v_pool = v_pool;
   p->block_table = block_table_dev;
@@ -669,6 +677,18 @@ int pa_create_pool(pa_pool** out, int num_blocks, int block_size, int num_kv_hea
       if (e != hipSuccess) {
         pa_destroy_pool(p);
         return hip_err(e, "hipEventCreate");
+      }
+    }
+  }
+  if (dtype == PA_FP8_E4M3) {
+    p->kv_scale_host.assign(4 * static_cast<size_t>(num_kv_heads), 1.0f);
+    if (!p->host_only) {
+      const size_t bytes = p->kv_scale_host.size() * sizeof(float);
+      hipError_t e = hipMalloc(&p->kv_scale, bytes);
+      if (e == hipSuccess) e = hipMemcpy(p->kv_scale, p->kv_scale_host.data(), bytes, hipMemcpyHostToDevice);
+      if (e != hipSuccess) {
+        pa_destroy_pool(p);
+        return hip_err(e, "E4M3 scales");
       }
     }
   }
@@ -687,9 +707,10 @@ int pa_destroy_pool(pa_pool* p) {
     hipEventDestroy(ev.start);
     hipEventDestroy(ev.stop);
   }
-  if (p->dplan || p->merge_ctr) hipDeviceSynchronize();
+  if (p->dplan || p->merge_ctr || p->kv_scale) hipDeviceSynchronize();
   if (p->dplan) hipFree(p->dplan);
   if (p->merge_ctr) hipFree(p->merge_ctr);
+  if (p->kv_scale) hipFree(p->kv_scale);
   delete p;
   return PA_OK;
 }
@@ -699,6 +720,30 @@ int pa_alloc_blocks(pa_pool* p, int seq_id, int parent_seq, int shared_tokens) {
   std::string err;
   int rc = p->bp.alloc(seq_id, parent_seq, shared_tokens, &err);
   return rc == pa::kOk ? PA_OK : set_err(rc, err);
+}
+
+int pa_set_kv_scales(pa_pool* p, const float* k_scale, const float* v_scale) {
+  if (!p || !k_scale || !v_scale) return set_err(PA_ERR_INVALID, "NULL argument");
+  if (p->dtype != PA_FP8_E4M3) return set_err(PA_ERR_STATE, "scales belong to PA_FP8_E4M3 pools");
+  const int h = p->hkv;
+  for (int i = 0; i < h; ++i)
+    if (!(k_scale[i] > 0.f) || !(v_scale[i] > 0.f) || !std::isfinite(k_scale[i]) || !std::isfinite(v_scale[i]))
+      return set_err(PA_ERR_INVALID, "scales must be finite and > 0");
+  std::vector<float> next(4 * static_cast<size_t>(h));
+  for (int i = 0; i < h; ++i) {
+    next[i] = k_scale[i];
+    next[h + i] = v_scale[i];
+    next[2 * h + i] = 1.0f / k_scale[i];
+    next[3 * h + i] = 1.0f / v_scale[i];
+  }
+  if (p->kv_scale) {
+    // the stream work already enqueued may still read the old scales
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemcpy(p->kv_scale, next.data(), next.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_err(e, "E4M3 scales");
+  }
+  p->kv_scale_host.swap(next);
+  return PA_OK;
 }
 
 int pa_append_kv(pa_pool* p, const int32_t* seq_ids, int n_seq, const int32_t* n_tok,
