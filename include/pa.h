@@ -164,15 +164,28 @@ int pa_decode(pa_pool* pool, const int32_t* seq_ids, int n_seq, int num_q_heads,
 
 /* Speculative verify: the last k_draft rows of each sequence are draft tokens
  * (already appended) and draft i (0-based) attends to positions
- * [0, length - k_draft + i], its own row included.
+ * [0, length - k_draft + i], its own row included (P1 section 1 and P2
+ * section 5.2, speculative decoding; P4 "Spéculer").
  *   q, out  device [n_seq][k_draft][num_q_heads][head_dim]
  *   lse     device float [n_seq][k_draft][num_q_heads] or NULL
- * (num_q_heads / num_kv_heads) * k_draft is at most 64 (32 when head_dim is
- * 256); lengths must be >= k_draft.  Other arguments as pa_decode.
+ * Lengths must be >= k_draft; (num_q_heads / num_kv_heads) * k_draft is at
+ * most 2^22.  A unit of work takes at most 64 query rows (32 when head_dim is
+ * 256); calls with more run one unit per tile of rows, and each tile reads
+ * only the positions its last row sees.  Other arguments as pa_decode.
  * k_draft = 1 is exactly pa_decode. */
 int pa_verify(pa_pool* pool, const int32_t* seq_ids, int n_seq, int k_draft, int num_q_heads,
               float scale, const void* q, void* out, float* lse, int partition_tokens,
               void* workspace, size_t ws_bytes, void* stream);
+
+/* Chunked prefill: the last n_new rows of each sequence are a chunk of its
+ * prompt (already appended, e.g. with pa_append_kv), and chunk token i
+ * (0-based) attends to positions [0, length - n_new + i].  Long prompts are
+ * split into such chunks so that their attention can run between decode steps
+ * (P4 "Les noyaux d'attention", chunked prefill).  The computation is exactly
+ * pa_verify with k_draft = n_new; q, out, lse, limits and errors as there.  */
+int pa_prefill(pa_pool* pool, const int32_t* seq_ids, int n_seq, int n_new, int num_q_heads,
+               float scale, const void* q, void* out, float* lse, int partition_tokens,
+               void* workspace, size_t ws_bytes, void* stream);
 
 /* pa_append_kv of n_new rows to each listed sequence followed by pa_verify
  * with k_draft = n_new (n_new = 1: pa_decode), issued as one kernel launch
@@ -180,7 +193,8 @@ int pa_verify(pa_pool* pool, const int32_t* seq_ids, int n_seq, int k_draft, int
  * takes the new rows straight from k_new / v_new.  Results are identical to
  * the two separate calls.  Falls back to two launches (same results) when a
  * write needs a copy-on-write copy first, when earlier table changes are still
- * pending, or for PA_F32 pools.
+ * pending, when (num_q_heads / num_kv_heads) * n_new is more than one unit's
+ * rows (see pa_verify), or for PA_F32 and PA_FP8_E4M3 pools.
  *   seq_ids  host int32 [n_seq]; live and distinct
  *   k_new, v_new  device [n_seq * n_new][num_kv_heads][head_dim], rows of
  *            sequence i at i * n_new .. i * n_new + n_new - 1

@@ -33,6 +33,8 @@ SIGNATURES = {
                           c_void_p, c_size_t, c_void_p]),
     "pa_verify": (c_int, [c_void_p, c_i32p, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p,
                           c_int, c_void_p, c_size_t, c_void_p]),
+    "pa_prefill": (c_int, [c_void_p, c_i32p, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p,
+                           c_int, c_void_p, c_size_t, c_void_p]),
     "pa_append_attend": (c_int, [c_void_p, c_i32p, c_int, c_int, c_void_p, c_void_p, c_int, c_float, c_void_p,
                                  c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
     "pa_truncate": (c_int, [c_void_p, c_int, c_int]),

@@ -197,6 +197,28 @@ class PagedKVCache:
         n_seq, kd, hq, d = q.shape
         return self._attend(seq_ids, kd, q, hq, scale, out, lse, want_lse, partition_tokens, workspace, stream)
 
+    def prefill(self, seq_ids, q: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, want_lse: bool = True, partition_tokens: int = 0,
+                workspace: Optional[torch.Tensor] = None, stream=None):
+        """Chunked prefill: q [n_seq, n_new, Hq, D] for the last n_new (already
+        appended) rows of each sequence; returns (out, lse)."""
+        if q.dim() != 4:
+            raise ValueError("q must be [n_seq, n_new, Hq, D]")
+        n_seq, n_new, hq, d = q.shape
+        if q.dtype != self.tdtype or not q.is_contiguous() or d != self.d:
+            raise ValueError("q must be contiguous, in the pool dtype, with the pool head_dim")
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None and want_lse:
+            lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+        ids, n = abi.i32_array(seq_ids)
+        if n != n_seq:
+            raise ValueError("one query set per sequence")
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        abi.check(self.lib.pa_prefill(self.handle, ids, n, n_new, hq, float(scale), _ptr(q), _ptr(out), _ptr(lse),
+                                      partition_tokens, _ptr(workspace), ws_bytes, _stream(stream)))
+        return out, lse
+
     def append_attend(self, seq_ids, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, scale: float,
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                       want_lse: bool = True, partition_tokens: int = 0,

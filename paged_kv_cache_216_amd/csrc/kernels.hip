@@ -298,6 +298,7 @@ __device__ inline void store_elem(T* p, float v) {
 // loads are issued, so that those loads do not wait for the length.
 struct Unit {
   int q_row, seq, n_raw, tok_begin, slot_base, nparts, part, merge, nlaunch;
+  int row0, trows;  // the unit's query rows: [row0, row0 + trows) of the call's rows
   int pre_row0, pre_member0, pre_rows;  // shared-prefix pass only
 };
 
@@ -311,6 +312,8 @@ __device__ inline Range resolve(const AttnParams& p, const Unit& u, int n_raw) {
   Range r;
   r.n = min(__builtin_amdgcn_readfirstlane(n_raw), p.max_blocks * kBlk);  // bounded by the table row
   r.tok_end = u.nparts > 1 ? min(r.n, u.tok_begin + p.part_tokens) : r.n;
+  // causal: no row of the unit sees past the last row's position
+  r.tok_end = min(r.tok_end, r.n - p.k_draft + (u.row0 + u.trows - 1) / p.group + 1);
   return r;
 }
 
@@ -479,7 +482,7 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       rr = r - j * rows;
       q_row = p.pre_members[u.pre_member0 + j].q_row;
     } else {
-      rr = min(nt * 16 + col, rows - 1);
+      rr = u.row0 + min(nt * 16 + col, u.trows - 1);
     }
     const int i = rr / G, g = rr - i * G;
     const T* qp = static_cast<const T*>(p.q) + (static_cast<size_t>(q_row * p.k_draft + i) * p.hq + kvh * G + g) * D;
@@ -502,7 +505,7 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
   for (int nt = 0; nt < NT; ++nt) {
     const int r = nt * 16 + col;
     // a shared prefix lies before every draft's first position: no causal limit
-    lim[nt] = PREFIX ? 0x7fffffff : n - p.k_draft + min(r, rows - 1) / G;
+    lim[nt] = PREFIX ? 0x7fffffff : n - p.k_draft + (u.row0 + min(r, u.trows - 1)) / G;
   }
 
   f32x4 acc[NT][DC];
@@ -515,7 +518,8 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
     for (int c = 0; c < DC; ++c) acc[nt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int mask_from = PREFIX ? 0x7fffffff : n - p.k_draft;  // positions above this may be masked for some row
+  // positions above this may be masked for some row
+  const int mask_from = PREFIX ? 0x7fffffff : n - p.k_draft + u.row0 / G;
   // Rows appended by this very launch (fused append) are not read from the
   // pool, which other workgroups of the launch are writing: the pool pass stops
   // at the last pair boundary before them, and a tail step processes the
@@ -846,8 +850,9 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int r = nt * 16 + 4 * grp + jj;
-        if (r < rows) {
-          const int i = r / G, g = r - (r / G) * G;
+        if (r < u.trows) {
+          const int rr = u.row0 + r;
+          const int i = rr / G, g = rr - (rr / G) * G;
           T* op = static_cast<T*>(p.out) +
                   (static_cast<size_t>(u.q_row * p.k_draft + i) * p.hq + kvh * G + g) * D;
 #pragma unroll
@@ -855,8 +860,9 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
         }
       }
       const int r = nt * 16 + col;
-      if (p.lse && grp == 0 && r < rows) {
-        const int i = r / G, g = r - (r / G) * G;
+      if (p.lse && grp == 0 && r < u.trows) {
+        const int rr = u.row0 + r;
+        const int i = rr / G, g = rr - (rr / G) * G;
         p.lse[static_cast<size_t>(u.q_row * p.k_draft + i) * p.hq + kvh * G + g] =
             (m_run[nt] + __builtin_amdgcn_logf(l)) * kLn2;
       }
@@ -868,8 +874,8 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int r = nt * 16 + 4 * grp + jj;
-        if (r < rows) {
-          float* ap = p.ws_acc + (static_cast<size_t>(slot) * rows + r) * D;
+        if (r < u.trows) {
+          float* ap = p.ws_acc + (static_cast<size_t>(slot) * rows + u.row0 + r) * D;
 #pragma unroll
           for (int c = 0; c < DC; ++c) {
             if constexpr (NT == 1)
@@ -880,8 +886,8 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
         }
       }
       const int r = nt * 16 + col;
-      if (grp == 0 && r < rows) {
-        float* mp = p.ws_ml + (static_cast<size_t>(slot) * rows + r) * 2;
+      if (grp == 0 && r < u.trows) {
+        float* mp = p.ws_ml + (static_cast<size_t>(slot) * rows + u.row0 + r) * 2;
         if constexpr (NT == 1) {
           store_device(mp, m_run[nt]);
           store_device(mp + 1, l);
@@ -916,8 +922,9 @@ __device__ inline void attn_body32(const AttnParams& p, const Unit& u, int kvh) 
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = nt * 16 + col;
-    if (r < rows) {
-      const int i = r / G, g = r - (r / G) * G;
+    if (r < u.trows) {
+      const int rr = u.row0 + r;
+      const int i = rr / G, g = rr - (rr / G) * G;
       const float* qp = static_cast<const float*>(p.q) +
                         (static_cast<size_t>(u.q_row * p.k_draft + i) * p.hq + kvh * G + g) * D;
 #pragma unroll
@@ -1020,8 +1027,9 @@ __device__ inline void attn_body32(const AttnParams& p, const Unit& u, int kvh) 
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int r = nt * 16 + 4 * grp + jj;
-        if (r < rows) {
-          const int i = r / G, g = r - (r / G) * G;
+        if (r < u.trows) {
+          const int rr = u.row0 + r;
+          const int i = rr / G, g = rr - (rr / G) * G;
           float* op = static_cast<float*>(p.out) +
                       (static_cast<size_t>(u.q_row * p.k_draft + i) * p.hq + kvh * G + g) * D;
 #pragma unroll
@@ -1029,8 +1037,9 @@ __device__ inline void attn_body32(const AttnParams& p, const Unit& u, int kvh) 
         }
       }
       const int r = nt * 16 + col;
-      if (p.lse && grp == 0 && r < rows) {
-        const int i = r / G, g = r - (r / G) * G;
+      if (p.lse && grp == 0 && r < u.trows) {
+        const int rr = u.row0 + r;
+        const int i = rr / G, g = rr - (rr / G) * G;
         p.lse[static_cast<size_t>(u.q_row * p.k_draft + i) * p.hq + kvh * G + g] =
             (m_run[nt] + __builtin_amdgcn_logf(l)) * kLn2;
       }
@@ -1039,15 +1048,15 @@ __device__ inline void attn_body32(const AttnParams& p, const Unit& u, int kvh) 
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int r = nt * 16 + 4 * grp + jj;
-        if (r < rows) {
-          float* ap = p.ws_acc + (static_cast<size_t>(slot) * rows + r) * D;
+        if (r < u.trows) {
+          float* ap = p.ws_acc + (static_cast<size_t>(slot) * rows + u.row0 + r) * D;
 #pragma unroll
           for (int c = 0; c < DC; ++c) ap[16 * c + col] = acc[nt][c][jj];
         }
       }
       const int r = nt * 16 + col;
-      if (grp == 0 && r < rows) {
-        float* mp = p.ws_ml + (static_cast<size_t>(slot) * rows + r) * 2;
+      if (grp == 0 && r < u.trows) {
+        float* mp = p.ws_ml + (static_cast<size_t>(slot) * rows + u.row0 + r) * 2;
         mp[0] = m_run[nt];
         mp[1] = l;
       }
@@ -1078,6 +1087,8 @@ __device__ inline void attn_unit(const AttnParams& p, const int32_t* meta) {
     u.n_raw = __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(lens, w.seq * 4, 0, 0));
   }
   u.tok_begin = w.nparts > 1 ? w.part * p.part_tokens : 0;
+  u.row0 = w.row0;
+  u.trows = min(p.tile_rows, p.rows - w.row0);
   if constexpr (std::is_same_v<T, float>)
     attn_body32<D, NT>(p, u, kvh);
   else
@@ -1134,6 +1145,8 @@ __global__ __launch_bounds__(64 * PrefixShape<D>::W) void prefix_kernel(AttnPara
   u.pre_row0 = row0;
   u.pre_member0 = pu.member0;
   u.pre_rows = pu.group_rows;
+  u.row0 = 0;
+  u.trows = 1 << 24;  // no causal limit: the prefix precedes every query row
   // the prefix blocks are read by every row block of the group: cached loads
   attn_body16<T, D, NT, false, false, true>(p, u, kvh);
 }
@@ -1233,7 +1246,7 @@ template <typename T, int D, bool NTL, bool Q8>
 hipError_t launch_attn_d(const AttnParams& p, const InlineMeta& m, hipStream_t stream) {
   // no fused fp32 or E4M3 path
   if ((std::is_same_v<T, float> || Q8) && p.t_new > 0) return hipErrorInvalidValue;
-  const int nt = (p.rows + 15) / 16;
+  const int nt = (p.tile_rows + 15) / 16;
   if (nt <= 1)
     launch_attn_nt<T, D, 1, NTL, Q8>(p, m, stream);
   else if (nt <= 2)

@@ -52,7 +52,8 @@ struct WorkUnit {
   int32_t part;       // partition index
   int32_t nparts;     // partitions of this sequence (1 = unsplit)
   int32_t slot_base;  // -1: write out/lse directly; else partial slot of kv head 0, part 0
-  int32_t pad0;       // length at plan time (host-side ordering only)
+  int32_t row0;       // first query row of the unit's tile: calls with more rows
+                      // than one unit takes (tile_rows) have one unit per tile
   int32_t merge;      // split sequences: index of its MergeUnit; else -1
   int32_t nlaunch;    // partitions of this sequence computed by this launch (the
                       // others, if any, by the shared-prefix pass before it)
@@ -108,6 +109,7 @@ struct AttnParams {
   int n_units;
   int n_merges;
   int hkv, hq, group, k_draft, rows;  // rows = group * k_draft
+  int tile_rows;      // query rows one unit takes: min(rows, max_rows_for_head_dim)
   int head_dim;
   float scale_log2;   // scale * log2(e)
   int stream_kv;      // 1: no block is shared, read K/V pages with the non-temporal hint
@@ -144,7 +146,8 @@ hipError_t launch_prefix(DType dt, const AttnParams& p, hipStream_t stream);
 int prefix_rows_per_unit(int head_dim);
 // Workgroups of 64 threads that the append work of `p` needs.
 int append_blocks64(const AppendParams& p);
-// Largest supported rows (group * k_draft) for a head dim.
+// Query rows one attention unit takes at most, for a head dim; calls with more
+// rows are split into tiles of this many rows.
 int max_rows_for_head_dim(int head_dim);
 
 }  // namespace pa

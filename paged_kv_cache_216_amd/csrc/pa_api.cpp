@@ -39,6 +39,9 @@ int hip_err(hipError_t e, const char* what) {
 
 constexpr int kStages = 64;
 constexpr int kDefaultPartition = 512;
+// query rows (group * queries per sequence) of one attention call; more than
+// one unit's worth are split into row tiles
+constexpr int64_t kMaxRows = int64_t{1} << 22;
 
 struct Stage {
   int32_t* host = nullptr;  // pinned, fine-grained (the GPU reads it without caching it)
@@ -85,7 +88,8 @@ struct pa_pool {
   pa::BlockPool::Dirty dirty;
   std::vector<int32_t> slots;
   std::vector<pa::CowCopy> cows;
-  std::vector<pa::WorkUnit> units, tail_units;
+  std::vector<pa::WorkUnit> units;
+  std::vector<std::pair<int, pa::WorkUnit>> tail_units;  // (tokens the unit reads, unit)
   std::vector<pa::MergeUnit> merges;
   std::vector<int> lens, parts;
   // shared-prefix pass: partitions of each sequence done by the pass (0 = none)
@@ -238,38 +242,50 @@ int64_t count_parts(pa_pool* p, int n_seq, int pt) {
   return slots;
 }
 
-// Work decomposition: one unit per (sequence, partition); units of split
-// sequences get consecutive partial slots (kv head major within a sequence).
-// Full-length units first, then the rest longest first (by the lengths at plan
-// time), so the grid's tail holds the short ones.
-void make_plan(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, int rows) {
+// Work decomposition: one unit per (sequence, partition, tile of query rows);
+// units of split sequences get consecutive partial slots (kv head major within
+// a sequence), shared by the sequence's row tiles.  Units that read a whole
+// partition first, then the rest by the tokens they read (causal limit
+// included), most first, so the grid's tail holds the short ones.
+void make_plan(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, int rows, int group, int k_draft) {
   std::vector<pa::WorkUnit>& units = p->units;
-  std::vector<pa::WorkUnit>& tail = p->tail_units;
+  auto& tail = p->tail_units;
   units.clear();
   tail.clear();
   p->merges.clear();
+  const int tr = std::min(rows, rows_limit(p));
   int64_t slots = 0;
   for (int i = 0; i < n_seq; ++i) {
     const int parts = p->parts[i];
-    if (parts == 1) {
-      tail.push_back({i, seq_ids[i], 0, 1, -1, p->lens[i], -1, 1});
-      continue;
-    }
-    const int base = static_cast<int>(slots);
-    const int merge = static_cast<int>(p->merges.size());
+    const int n = p->lens[i];
+    const int base = parts == 1 ? -1 : static_cast<int>(slots);
+    const int merge = parts == 1 ? -1 : static_cast<int>(p->merges.size());
     const int q0 = p->pre_parts[i];  // partitions done by the shared-prefix pass
-    slots += static_cast<int64_t>(parts) * p->hkv;
-    for (int q = q0; q < parts; ++q) {
-      const int len = std::min(p->lens[i], (q + 1) * pt) - q * pt;
-      (len == pt ? units : tail).push_back({i, seq_ids[i], q, parts, base, len, merge, parts - q0});
+    if (parts > 1) slots += static_cast<int64_t>(parts) * p->hkv;
+    for (int row0 = 0; row0 < rows; row0 += tr) {
+      const int last_row = std::min(rows, row0 + tr) - 1;
+      const int visible = n - k_draft + last_row / group + 1;  // tokens the tile's last row sees
+      if (parts == 1) {
+        tail.push_back({std::min(n, visible), {i, seq_ids[i], 0, 1, -1, row0, -1, 1}});
+        continue;
+      }
+      for (int q = q0; q < parts; ++q) {
+        const int len = std::max(0, std::min({n, (q + 1) * pt, visible}) - q * pt);
+        const pa::WorkUnit u{i, seq_ids[i], q, parts, base, row0, merge, parts - q0};
+        if (len == pt)
+          units.push_back(u);
+        else
+          tail.push_back({len, u});
+      }
     }
-    p->merges.push_back({i, base, parts, 0});
+    if (parts > 1) p->merges.push_back({i, base, parts, 0});
   }
-  // pad0 holds the unit's length at plan time, used only for this ordering
-  std::sort(tail.begin(), tail.end(), [](const pa::WorkUnit& a, const pa::WorkUnit& b) {
-    return a.pad0 != b.pad0 ? a.pad0 > b.pad0 : (a.q_row != b.q_row ? a.q_row < b.q_row : a.part < b.part);
+  std::sort(tail.begin(), tail.end(), [](const auto& a, const auto& b) {
+    if (a.first != b.first) return a.first > b.first;
+    if (a.second.q_row != b.second.q_row) return a.second.q_row < b.second.q_row;
+    return a.second.part != b.second.part ? a.second.part < b.second.part : a.second.row0 < b.second.row0;
   });
-  units.insert(units.end(), tail.begin(), tail.end());
+  for (const auto& t : tail) units.push_back(t.second);
   p->plan_slots = slots;
   p->plan_max_parts = 0;
   for (const pa::MergeUnit& m : p->merges) p->plan_max_parts = std::max(p->plan_max_parts, m.nparts);
@@ -432,8 +448,8 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
     return set_err(PA_ERR_INVALID, "num_q_heads must be a positive multiple of num_kv_heads");
   const int group = num_q_heads / p->hkv;
   const int64_t rows64 = static_cast<int64_t>(group) * k_draft;
-  if (rows64 > rows_limit(p))
-    return set_err(PA_ERR_INVALID, "(num_q_heads / num_kv_heads) * k_draft exceeds the supported rows");
+  if (rows64 > kMaxRows)
+    return set_err(PA_ERR_INVALID, "(num_q_heads / num_kv_heads) * k_draft exceeds 2^22 query rows");
   const int rows = static_cast<int>(rows64);
   if (partition_tokens < 0 || (partition_tokens > 0 && partition_tokens % 32 != 0))
     return set_err(PA_ERR_INVALID, "partition_tokens must be 0 or a positive multiple of 32");
@@ -484,7 +500,10 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
     // attention reads the table while the launch's append work writes it, which
     // is safe only for the blocks this append opens (their only valid rows are
     // the new ones, which the attention takes from k_new / v_new).
-    fused = p->cows.empty() && !table_pending && (p->dtype == PA_F16 || p->dtype == PA_BF16);
+    // (a call with several row tiles appends first: each tile would splice
+    // the new rows again)
+    fused = p->cows.empty() && !table_pending && (p->dtype == PA_F16 || p->dtype == PA_BF16) &&
+            rows <= rows_limit(p);
     if (!fused) {
       p->bp.take_dirty(&p->dirty);
       rc = launch_append_call(p, app->k_new, app->v_new, stream);
@@ -509,7 +528,7 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
     key.push_back(p->pre_parts[i]);
   }
   if (key != p->plan_key) {
-    make_plan(p, seq_ids, n_seq, pt, rows);
+    make_plan(p, seq_ids, n_seq, pt, rows, group, k_draft);
     const size_t w_units = 8 * p->units.size(), w_merges = 4 * p->merges.size();
     const size_t w_pre = 8 * p->pre_units.size(), w_mem = 4 * p->pre_members.size();
     const size_t plan_words = w_units + w_merges + w_pre + w_mem;
@@ -565,6 +584,7 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   ak.group = group;
   ak.k_draft = k_draft;
   ak.rows = rows;
+  ak.tile_rows = std::min(rows, rows_limit(p));
   ak.head_dim = p->head_dim;
   ak.scale_log2 = scale * 1.4426950408889634f;
   ak.stream_kv = p->bp.num_shared() == 0 ? 1 : 0;
@@ -777,6 +797,13 @@ int pa_verify(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int nu
               const void* q, void* out, float* lse, int partition_tokens, void* workspace,
               size_t ws_bytes, void* stream) {
   return attend(p, seq_ids, n_seq, k_draft, num_q_heads, scale, q, out, lse, partition_tokens, workspace,
+                ws_bytes, stream, nullptr);
+}
+
+int pa_prefill(pa_pool* p, const int32_t* seq_ids, int n_seq, int n_new, int num_q_heads, float scale,
+               const void* q, void* out, float* lse, int partition_tokens, void* workspace, size_t ws_bytes,
+               void* stream) {
+  return attend(p, seq_ids, n_seq, n_new, num_q_heads, scale, q, out, lse, partition_tokens, workspace,
                 ws_bytes, stream, nullptr);
 }
 
