@@ -30,7 +30,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "paged-attn decode effective HBM GB/s (% of MI355X peak); µs/step at batch 256"
+METRIC_PREFILL = "paged-attn chunked-prefill attention TFLOP/s (% of MI355X dense bf16/fp16 MFMA peak)"
 PEAK_GBS = 8000.0  # MI355X HBM3E, AMD public specification
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # dense MFMA (fp32: vector), AMD public figures
 FILL = {"f32": 0x7FBADBAD, "f16": 0x7E5A, "bf16": 0x7FDA, "fp8": 0x7F}
 EB = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 
@@ -40,9 +42,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="highbatch", choices=["highbatch", "gqa70b", "long", "verify", "tiny"])
+    ap.add_argument("--workload", default="highbatch",
+                    choices=["highbatch", "gqa70b", "long", "verify", "tiny", "prefill"])
     ap.add_argument("--replicas", type=int, default=4)
-    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--partition-tokens", type=int, default=0,
+                    help="split-KV partition length; 0: the workload's (or the library's) choice; -1: no split")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--kv-cache", default="same", choices=["same", "fp8"],
                     help="pool element type: the workload's own, or E4M3 codes with one scale per kv head "
@@ -86,6 +90,23 @@ def decode_bytes(w, kv_eb) -> int:
     qo = 2 * len(lens) * w.k_draft * w.num_q_heads * w.head_dim * e
     tab = sum(math.ceil(n / 16) for n in lens) * 4 + 4 * len(lens)
     return kv + qo + tab
+
+
+def is_prefill(w) -> bool:
+    """Many query tokens per sequence: the attention is bound by the matrix
+    cores, not by HBM, and is reported in TFLOP/s."""
+    return w.k_draft >= 64
+
+
+def attention_flops(w) -> int:
+    """Multiply-add work of the attention: every query row of every query head
+    against each position it sees, 2 D flops for QK and 2 D for PV."""
+    lens = step_lengths(w)
+    seen = 0
+    for n in lens:
+        first = n - w.k_draft + 1  # positions the first query sees
+        seen += w.k_draft * first + w.k_draft * (w.k_draft - 1) // 2
+    return 4 * w.head_dim * w.num_q_heads * seen
 
 
 def append_bytes(w, kv_eb) -> int:
@@ -159,7 +180,10 @@ class Replica:
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty(self.q.shape[:-1], dtype=torch.float32, device="cuda")
         max_len = max(step_lengths(w))
-        self.ws = c.make_workspace(b, w.num_q_heads, max_len, k_draft=w.k_draft, partition_tokens=pt)
+        # pt < 0: no workspace, so nothing splits
+        self.ws = None if pt < 0 else c.make_workspace(b, w.num_q_heads, max_len, k_draft=w.k_draft,
+                                                       partition_tokens=pt)
+        pt = max(pt, 0)
         self.ws_bytes = 0 if self.ws is None else self.ws.numel() * 4
         self.pt = pt
         self.separate = separate
@@ -206,7 +230,9 @@ def describe(w) -> str:
          "long": "8 seqs x 32768 tokens, 32 q / 8 kv heads, head_dim 128, fp16, 512-token split-KV; step = decode",
          "verify": "64 seqs sharing a 4096-token copy-on-write prefix + suffix U[16, 512], 32 q / 8 kv heads, "
                    "head_dim 128, bf16; step = append 5 drafts/seq + causal verify",
-         "tiny": "4 seqs {17, 33, 64, 100}, 4 heads, head_dim 64, fp32; step = append + decode"}
+         "tiny": "4 seqs {17, 33, 64, 100}, 4 heads, head_dim 64, fp32; step = append + decode",
+         "prefill": "4 seqs x 8192 cached prompt tokens + a 512-token chunk each, 32 q / 8 kv heads, head_dim 128, "
+                    "bf16; step = append the chunk + causal chunk attention"}
     return d[w.name]
 
 
@@ -219,7 +245,7 @@ def cpu_baseline(w, budget_s, cache_dtype, scales):
     from oracle.allocator import PoolModel
 
     lens = step_lengths(w)
-    done_bytes, elapsed, nseq, ntok = 0, 0.0, 0, 0
+    done_bytes, done_flops, elapsed, nseq, ntok = 0, 0, 0.0, 0, 0
     with threadpool_limits(limits=1):
         for s in range(w.batch):
             m = PoolModel(w.num_blocks, w.num_kv_heads, w.head_dim, cache_dtype, 1, w.max_blocks_per_seq,
@@ -246,12 +272,18 @@ def cpu_baseline(w, budget_s, cache_dtype, scales):
             n = lens[s]
             done_bytes += (n * w.num_kv_heads * w.head_dim * EB[cache_dtype] * 2
                            + 2 * w.k_draft * w.num_q_heads * w.head_dim * EB[w.dtype] + math.ceil(n / 16) * 4 + 4)
+            done_flops += 4 * w.head_dim * w.num_q_heads * (w.k_draft * (n - w.k_draft + 1)
+                                                            + w.k_draft * (w.k_draft - 1) // 2)
             nseq += 1
             ntok += n
             if elapsed >= budget_s:
                 break
+    if is_prefill(w):
+        value, unit = done_flops / elapsed / 1e12, "TFLOP/s"
+    else:
+        value, unit = done_bytes / elapsed / 1e9, "GB/s"
     return {
-        "value": round(done_bytes / elapsed / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "value": round(value, 6), "unit": unit, "cores": 1, "kind": "oracle",
         "sample": f"first {nseq} of {w.batch} sequences ({ntok} cached tokens): append into the float64 "
                   f"oracle's pool model, then gather + softmax attention; one thread; {elapsed:.1f} s",
         "cpu": platform.processor() or platform.machine(), "host_cpus": os.cpu_count(),
@@ -374,9 +406,16 @@ def main():
     dec_b = decode_bytes(w, EB[cd])
     app_b = append_bytes(w, EB[cd])
     step_b = dec_b + app_b
+    flops = attention_flops(w)
+    prefill = is_prefill(w)
     value = step_b / (ms_step * 1e-3) / 1e9
+    if prefill:
+        value = flops / (ms_step * 1e-3) / 1e12
     # 8-bit pools take the append and the attention as two launches
-    fused = bool(reps[0].t_new) and not args.separate and cd != "fp8"
+    # 8-bit pools and calls of several row tiles take the append and the
+    # attention as two launches
+    one_tile = (w.num_q_heads // w.num_kv_heads) * w.k_draft <= (64 if w.head_dim <= 128 else 32)
+    fused = bool(reps[0].t_new) and not args.separate and cd != "fp8" and one_tile
     roof = None
     if kern[0][1]:
         attn_ms = kern[0][0] / kern[0][1]
@@ -388,17 +427,27 @@ def main():
                 "frac": round(achieved / PEAK_GBS, 4), "traffic": measured_traffic(wkey, kname),
                 "kernel": kname, "avg_us": round(attn_ms * 1e3, 2), "bytes_per_launch": launch_b,
                 "timing": "HIP events around each launch on its stream, over a second pass of the timed steps"}
+        if prefill:
+            # the shared-prefix pass does not run here; the merge launch is
+            # reported in kernel_us
+            tf = flops / (attn_ms * 1e-3) / 1e12
+            peak = PEAK_TFLOPS[w.dtype]
+            roof.update({"bound": "mfma", "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
+                         "frac": round(tf / peak, 4), "flops_per_launch": flops,
+                         "hbm_gbs": round(achieved, 1)})
     line = {
-        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC_PREFILL if prefill else METRIC, "value": round(value, 2),
+        "unit": "TFLOP/s" if prefill else "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "us_per_step": round(ms_step * 1e3, 2),
-        "pct_of_peak": round(100 * value / PEAK_GBS, 2), "higher_is_better": True, "scaling": "weak",
+        "pct_of_peak": round(100 * value / (PEAK_TFLOPS[w.dtype] if prefill else PEAK_GBS), 2), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"{wkey}: {describe(w)}" + (
                        "; key/value pools in E4M3 with one scale per kv head (amax / 448)" if cd == "fp8" else ""),
                    "kv_cache": cd, "batch": w.batch, "seed": w.seed,
-                   "replicas": args.replicas, "partition_tokens": pt or "library choice (512 when split)",
+                   "replicas": args.replicas,
+                   "partition_tokens": pt if pt > 0 else ("unsplit" if pt < 0 else "library choice"),
                    "bytes_per_step": step_b, "decode_bytes": dec_b, "append_bytes": app_b,
-                   "cached_tokens": int(sum(step_lengths(w)))},
+                   "cached_tokens": int(sum(step_lengths(w))), "attention_flops": flops},
         "kernel_us": {"attention": round(1e3 * kern[0][0] / max(1, kern[0][1]), 2),
                       "merge": round(1e3 * kern[1][0] / max(1, kern[1][1]), 2) if kern[1][1] else None,
                       "append": round(1e3 * kern[2][0] / max(1, kern[2][1]), 2) if kern[2][1] else None,

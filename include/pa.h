@@ -133,16 +133,16 @@ int pa_append_kv(pa_pool* pool, const int32_t* seq_ids, int n_seq, const int32_t
 /* One query token per sequence attends over all of its cached tokens.
  *   seq_ids      host int32 [n_seq]; live, length >= 1 (repeats allowed)
  *   num_q_heads  multiple of num_kv_heads; query head h reads key/value head
- *                h / (num_q_heads / num_kv_heads); (num_q_heads/num_kv_heads)
- *                at most 64 (32 when head_dim is 256)
+ *                h / (num_q_heads / num_kv_heads)
  *   scale        multiplies q.k before the softmax (typically 1/sqrt(head_dim))
  *   q, out       device [n_seq][num_q_heads][head_dim] in dtype
  *   lse          device float [n_seq][num_q_heads] (natural-log log-sum-exp of
  *                the scaled scores) or NULL
- *   partition_tokens  0 = library choice; otherwise a positive multiple of 32:
- *                contexts longer than this are cut into partitions processed
- *                in parallel and merged exactly by their log-sum-exp; a value
- *                >= the longest context disables the split
+ *   partition_tokens  0 = library choice (512 tokens, or 8 per query row
+ *                of a kv head when that is more); otherwise a positive
+ *                multiple of 32: contexts longer than this are cut into
+ *                partitions processed in parallel and merged exactly by their
+ *                log-sum-exp; a value >= the longest context disables the split
  *   workspace    device scratch for split partials, ws_bytes long (see
  *                pa_workspace_size); may be NULL when no sequence is split.
  *                With partition_tokens = 0 the library only splits when the

@@ -549,6 +549,7 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
     const bool need_mask = (pos0 + 2 * kBlk - 1 > mask_from) || (pos0 + 2 * kBlk > end);
     Op pa[NT];
     float a4[NT][4];
+    bool rescale[NT];
     // scores and online-softmax update for every row tile (needs K only)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -588,9 +589,16 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       }
       l_run[nt] = l_run[nt] * alpha + ps;
       m_run[nt] = m_new;
+      // Once the running maxima settle, alpha is exactly 1 on every row and the
+      // accumulator rescale (a multiply by 1) is skipped for the whole wave.
+      // (Single-tile waves only: with more tiles the branch costs more than the
+      // multiplies it saves, measured on MI355X.)
+      rescale[nt] = NT > 1 || __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0;
       // rescale factors move to the accumulator layout: lane holds rows 4*grp + jj
+      if (rescale[nt]) {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) a4[nt][jj] = shfl_f(alpha, 4 * grp + jj);
+        for (int jj = 0; jj < 4; ++jj) a4[nt][jj] = shfl_f(alpha, 4 * grp + jj);
+      }
     }
     if (pos0 + 2 * kBlk > end) {
 #pragma unroll
@@ -602,10 +610,14 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
     // O = diag(alpha) O + P V
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
+      if (rescale[nt]) {
+#pragma unroll
+        for (int c = 0; c < DC; ++c)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) acc[nt][c][jj] *= a4[nt][jj];
+      }
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[nt][c][jj] *= a4[nt][jj];
         const Op vb = __builtin_bit_cast(Op, u32x4{f.v0[c][0], f.v0[c][1], f.v1[c][0], f.v1[c][1]});
         acc[nt][c] = MfmaOp<T>::mma(pa[nt], vb, acc[nt][c]);
       }

@@ -39,6 +39,14 @@ int hip_err(hipError_t e, const char* what) {
 
 constexpr int kStages = 64;
 constexpr int kDefaultPartition = 512;
+// The library's partition length for a call with `rows` query rows per kv
+// head: 512 tokens, or 8 tokens per row when that is more, so that the split
+// partials (rows x (D + 2) floats per partition) stay within an eighth of the
+// key/value bytes the partition reads.
+int default_partition(int64_t rows) {
+  const int64_t pt = std::max<int64_t>(kDefaultPartition, (8 * rows + 31) / 32 * 32);
+  return static_cast<int>(std::min<int64_t>(pt, int64_t{1} << 30));
+}
 // query rows (group * queries per sequence) of one attention call; more than
 // one unit's worth are split into row tiles
 constexpr int64_t kMaxRows = int64_t{1} << 22;
@@ -472,7 +480,7 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   int pt = partition_tokens;
   int64_t slots;
   if (pt == 0) {
-    pt = kDefaultPartition;
+    pt = default_partition(rows);
     slots = count_parts(p, n_seq, pt);
     if (slots && (!workspace || plan_ws_bytes(p, slots, rows) > ws_bytes)) {
       pt = 0;  // the workspace cannot hold the split: run unsplit
@@ -858,9 +866,9 @@ int pa_workspace_size(const pa_pool* p, int n_seq, int num_q_heads, int k_draft,
     return set_err(PA_ERR_INVALID, "bad sizes");
   if (partition_tokens < 0 || (partition_tokens > 0 && partition_tokens % 32))
     return set_err(PA_ERR_INVALID, "partition_tokens must be 0 or a positive multiple of 32");
-  const int pt = partition_tokens == 0 ? kDefaultPartition : partition_tokens;
-  const int64_t parts = max_tokens > pt ? (max_tokens + pt - 1) / pt : 0;
   const int64_t rows = static_cast<int64_t>(num_q_heads / p->hkv) * k_draft;
+  const int pt = partition_tokens == 0 ? default_partition(rows) : partition_tokens;
+  const int64_t parts = max_tokens > pt ? (max_tokens + pt - 1) / pt : 0;
   *bytes = static_cast<size_t>(n_seq) * parts * p->hkv * rows * (p->head_dim + 2) * sizeof(float);
   return PA_OK;
 }

@@ -13,6 +13,7 @@ from .synth import (  # noqa: F401
     make_highbatch,
     make_long,
     make_verify,
+    make_prefill,
     make_custom,
     by_name,
 )

@@ -204,7 +204,7 @@ def make_custom(
     )
 
 
-# ---- the five named workloads -------------------------------------------------
+# ---- the named workloads -------------------------------------------------
 
 def make_tiny(seed: int = 1) -> Workload:
     """4 sequences of {17, 33, 64, 100} tokens, 4 heads (no grouping), D=64, fp32,
@@ -268,9 +268,19 @@ def make_verify(seed: int = 5, batch: int = 64, prefix_len: int = 4096,
     )
 
 
+def make_prefill(seed: int = 6, batch: int = 4, cached: int = 8192, chunk: int = 512) -> Workload:
+    """Chunked prefill of long prompts: 4 sequences hold 8,192 prompt tokens
+    from earlier chunks and take their next 512-token chunk (each chunk token
+    attends causally); 32 query / 8 KV heads, D=128, bf16."""
+    return make_custom(
+        name="prefill", mode="verify", lengths=[cached] * batch, num_q_heads=32, num_kv_heads=8,
+        head_dim=128, dtype="bf16", seed=seed, k_draft=chunk,
+    )
+
+
 def by_name(name: str, **kw) -> Workload:
     table = {
         "tiny": make_tiny, "gqa70b": make_gqa70b, "highbatch": make_highbatch,
-        "long": make_long, "verify": make_verify,
+        "long": make_long, "verify": make_verify, "prefill": make_prefill,
     }
     return table[name](**kw)
