@@ -298,7 +298,8 @@ __device__ inline void store_elem(T* p, float v) {
 // loads are issued, so that those loads do not wait for the length.
 struct Unit {
   int q_row, seq, n_raw, tok_begin, slot_base, nparts, part, merge, nlaunch;
-  int row0, trows;  // the unit's query rows: [row0, row0 + trows) of the call's rows
+  int row0, trows;  // this wave's query rows: [row0, row0 + trows) of the call's rows
+  int clip_row;     // the last row of the workgroup: no position past what it sees is read
   int pre_row0, pre_member0, pre_rows;  // shared-prefix pass only
 };
 
@@ -313,7 +314,7 @@ __device__ inline Range resolve(const AttnParams& p, const Unit& u, int n_raw) {
   r.n = min(__builtin_amdgcn_readfirstlane(n_raw), p.max_blocks * kBlk);  // bounded by the table row
   r.tok_end = u.nparts > 1 ? min(r.n, u.tok_begin + p.part_tokens) : r.n;
   // causal: no row of the unit sees past the last row's position
-  r.tok_end = min(r.tok_end, r.n - p.k_draft + (u.row0 + u.trows - 1) / p.group + 1);
+  r.tok_end = min(r.tok_end, r.n - p.k_draft + u.clip_row / p.group + 1);
   return r;
 }
 
@@ -444,9 +445,15 @@ __device__ inline uint32_t page_load4(__amdgpu_buffer_rsrc_t r, int byte_off) {
 // Q8: the pool holds E4M3 codes (T is bf16): K and V are loaded at one byte
 // per element, converted exactly to bf16 in registers, and the per-head
 // scales fold into the score scale (K) and the output (V).
-template <typename T, int D, int NT, bool NTL, bool FUSED, bool PREFIX = false, bool Q8 = false>
+// W > 1: the workgroup's W waves take consecutive row blocks of one unit and
+// share each pair of blocks through LDS: the pair is fetched once, 16 bytes
+// per thread, into one of two LDS buffers while the waves compute on the
+// other.  All W waves run the same pair loop (the unit's range is the
+// workgroup's), so the barriers line up.
+template <typename T, int D, int NT, bool NTL, bool FUSED, bool PREFIX = false, bool Q8 = false, int W = 1>
 __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) {
   static_assert(!(Q8 && (FUSED || PREFIX)), "E4M3 pools take the plain path");
+  static_assert(W == 1 || !(Q8 || FUSED || PREFIX), "LDS-shared pairs: plain 16-bit path only");
   using Op = typename MfmaOp<T>::type;
   constexpr int KS = D / 32;  // QK k-steps per block
   constexpr int DC = D / 16;  // output dim chunks
@@ -591,9 +598,10 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       m_run[nt] = m_new;
       // Once the running maxima settle, alpha is exactly 1 on every row and the
       // accumulator rescale (a multiply by 1) is skipped for the whole wave.
-      // (Single-tile waves only: with more tiles the branch costs more than the
-      // multiplies it saves, measured on MI355X.)
-      rescale[nt] = NT > 1 || __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0;
+      // (Measured on MI355X: pays for single-tile waves and for the LDS-shared
+      // workgroups of long row tiles; costs more than it saves for the
+      // multi-tile single waves of verify and the shared-prefix pass.)
+      rescale[nt] = (NT > 1 && W == 1) || __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0;
       // rescale factors move to the accumulator layout: lane holds rows 4*grp + jj
       if (rescale[nt]) {
 #pragma unroll
@@ -690,7 +698,65 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
     // dependent access (measured on MI355X: 3-6 % faster than keeping two
     // pairs in flight).  Multi-tile (verify) waves do more math per pair and
     // keep the second pair in flight.
-    if constexpr (Q8) {
+    if constexpr (W > 1) {
+      // pair image in LDS: [K block 0][K block 1][V block 0][V block 1], each
+      // page as laid out in the pool, so fragments are read at pool offsets
+      constexpr int kPair = 4 * kPageBytes;
+      constexpr int kPer = kPair / (16 * 64 * W);  // 16-byte chunks per thread
+      static_assert(kPer * 16 * 64 * W == kPair, "pair image must split evenly");
+      __shared__ __attribute__((aligned(16))) char lds[2][kPair];
+      const int tid = threadIdx.x;
+      u32x4 st[kPer];
+      auto gload = [&](int pj) {
+        const int j = 2 * pj;
+        const int bytes0 = j < cnt ? kPageBytes : 0;
+        const int bytes1 = j + 1 < cnt ? kPageBytes : 0;
+        const size_t off0 = (static_cast<size_t>(phys_at(min(j, cnt - 1))) * p.hkv + kvh) * page;
+        const size_t off1 = (static_cast<size_t>(phys_at(min(j + 1, cnt - 1))) * p.hkv + kvh) * page;
+        const __amdgpu_buffer_rsrc_t rs[4] = {page_rsrc(kpool + off0, bytes0), page_rsrc(kpool + off1, bytes1),
+                                              page_rsrc(vpool + off0, bytes0), page_rsrc(vpool + off1, bytes1)};
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+          const int ci = tid + 64 * W * k;  // chunk of the pair image
+          const int pg = ci / (kPageBytes / 16);
+          st[k] = page_load16<NTL>(rs[pg], (ci - pg * (kPageBytes / 16)) * 16);
+        }
+      };
+      auto lstore = [&](int b) {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+          *reinterpret_cast<u32x4*>(&lds[b][(tid + 64 * W * k) * 16]) = st[k];
+      };
+      auto lfrag = [&](Frag& f, int b) {
+        const char* kb = lds[b];
+        const char* vb = lds[b] + 2 * kPageBytes;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const int o = ((4 * s + grp) * kBlk + col) * 16;
+          f.k0[s] = __builtin_bit_cast(Op, *reinterpret_cast<const u32x4*>(kb + o));
+          f.k1[s] = __builtin_bit_cast(Op, *reinterpret_cast<const u32x4*>(kb + kPageBytes + o));
+        }
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          const int o = ((16 * c + col) * kBlk + 4 * grp) * 2;
+          f.v0[c] = *reinterpret_cast<const u32x2*>(vb + o);
+          f.v1[c] = *reinterpret_cast<const u32x2*>(vb + kPageBytes + o);
+        }
+      };
+      if (npairs > 0) {
+        gload(0);
+        lstore(0);
+        __syncthreads();
+      }
+      for (int pj = 0; pj < npairs; ++pj) {
+        if (pj + 1 < npairs) gload(pj + 1);
+        Frag f;
+        lfrag(f, pj & 1);
+        process(f, base_pos + 2 * pj * kBlk, pool_end);
+        if (pj + 1 < npairs) lstore((pj + 1) & 1);
+        __syncthreads();
+      }
+    } else if constexpr (Q8) {
       auto run = [&](Frag8& r, int pos0) {
         Frag f;
 #pragma unroll
@@ -1101,6 +1167,7 @@ __device__ inline void attn_unit(const AttnParams& p, const int32_t* meta) {
   u.tok_begin = w.nparts > 1 ? w.part * p.part_tokens : 0;
   u.row0 = w.row0;
   u.trows = min(p.tile_rows, p.rows - w.row0);
+  u.clip_row = u.row0 + u.trows - 1;
   if constexpr (std::is_same_v<T, float>)
     attn_body32<D, NT>(p, u, kvh);
   else
@@ -1110,6 +1177,45 @@ __device__ inline void attn_unit(const AttnParams& p, const int32_t* meta) {
 template <typename T, int D, int NT, bool NTL, bool Q8 = false>
 __global__ __launch_bounds__(64) void attn_kernel(AttnParams p) {
   attn_unit<T, D, NT, NTL, false, Q8>(p, nullptr);
+}
+
+// Many query rows per (sequence, kv head) -- chunked prefill, long verify --
+// take workgroups of TileShape::W waves, each wave 16 * NT consecutive rows of
+// the workgroup's tile, the waves sharing every pair of blocks through LDS.
+template <int D>
+struct TileShape {
+  static constexpr int NT = D <= 128 ? 2 : 1;  // row tiles per wave
+  static constexpr int W = 4;                  // waves per workgroup
+  static constexpr int kRows = 16 * NT * W;    // query rows per workgroup
+};
+
+template <typename T, int D, bool NTL>
+__global__ __launch_bounds__(64 * TileShape<D>::W) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
+void tile_kernel(AttnParams p) {
+  constexpr int NT = TileShape<D>::NT, W = TileShape<D>::W;
+  const int unit = blockIdx.x / p.hkv;
+  const int kvh = blockIdx.x - unit * p.hkv;
+  const WorkUnit w = p.units[unit];
+  const int wave = threadIdx.x >> 6;
+  Unit u{};
+  u.q_row = w.q_row;
+  u.seq = w.seq;
+  u.slot_base = w.slot_base;
+  u.nparts = w.nparts;
+  u.part = w.part;
+  u.merge = w.merge;
+  u.nlaunch = w.nlaunch;
+  const auto lens = page_rsrc(p.seq_len, 0x7ffffff0);
+  u.n_raw = __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(lens, w.seq * 4, 0, 0));
+  u.tok_begin = w.nparts > 1 ? w.part * p.part_tokens : 0;
+  const int g_rows = min(p.tile_rows, p.rows - w.row0);
+  u.row0 = w.row0 + wave * 16 * NT;
+  // a wave past the tile's rows (trows <= 0) still loads its share of every
+  // pair and meets every barrier; its queries repeat the tile's last row and
+  // nothing of it is stored
+  u.trows = min(16 * NT, g_rows - wave * 16 * NT);
+  u.clip_row = w.row0 + g_rows - 1;
+  attn_body16<T, D, NT, NTL, false, false, false, W>(p, u, kvh);
 }
 
 // Attention and append in one launch: workgroups past the attention grid do
@@ -1159,6 +1265,7 @@ __global__ __launch_bounds__(64 * PrefixShape<D>::W) void prefix_kernel(AttnPara
   u.pre_rows = pu.group_rows;
   u.row0 = 0;
   u.trows = 1 << 24;  // no causal limit: the prefix precedes every query row
+  u.clip_row = 1 << 24;
   // the prefix blocks are read by every row block of the group: cached loads
   attn_body16<T, D, NT, false, false, true>(p, u, kvh);
 }
@@ -1258,6 +1365,14 @@ template <typename T, int D, bool NTL, bool Q8>
 hipError_t launch_attn_d(const AttnParams& p, const InlineMeta& m, hipStream_t stream) {
   // no fused fp32 or E4M3 path
   if ((std::is_same_v<T, float> || Q8) && p.t_new > 0) return hipErrorInvalidValue;
+  if constexpr (!std::is_same_v<T, float> && !Q8) {
+    if (p.tile_rows > max_rows_for_head_dim(D)) {
+      if (p.tile_rows != TileShape<D>::kRows || p.t_new > 0) return hipErrorInvalidValue;
+      const dim3 grid(static_cast<unsigned>(p.n_units) * p.hkv);
+      hipLaunchKernelGGL((tile_kernel<T, D, NTL>), grid, dim3(64 * TileShape<D>::W), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
   const int nt = (p.tile_rows + 15) / 16;
   if (nt <= 1)
     launch_attn_nt<T, D, 1, NTL, Q8>(p, m, stream);
@@ -1286,6 +1401,17 @@ hipError_t launch_attn_t(const AttnParams& p, const InlineMeta& m, hipStream_t s
 }  // namespace
 
 int max_rows_for_head_dim(int head_dim) { return head_dim <= 128 ? 64 : 32; }
+
+int tile_rows_for_call(int dtype, int head_dim, int rows) {
+  const int one_wave = max_rows_for_head_dim(head_dim);
+  if (rows <= one_wave) return rows;
+  if (dtype != kF16 && dtype != kBF16) return one_wave;  // fp32 and E4M3: single-wave tiles
+  switch (head_dim) {
+    case 64: return TileShape<64>::kRows;
+    case 128: return TileShape<128>::kRows;
+    default: return TileShape<256>::kRows;
+  }
+}
 
 int prefix_rows_per_unit(int head_dim) {
   switch (head_dim) {

@@ -109,7 +109,7 @@ struct AttnParams {
   int n_units;
   int n_merges;
   int hkv, hq, group, k_draft, rows;  // rows = group * k_draft
-  int tile_rows;      // query rows one unit takes: min(rows, max_rows_for_head_dim)
+  int tile_rows;      // query rows one unit takes (tile_rows_for_call)
   int head_dim;
   float scale_log2;   // scale * log2(e)
   int stream_kv;      // 1: no block is shared, read K/V pages with the non-temporal hint
@@ -146,8 +146,11 @@ hipError_t launch_prefix(DType dt, const AttnParams& p, hipStream_t stream);
 int prefix_rows_per_unit(int head_dim);
 // Workgroups of 64 threads that the append work of `p` needs.
 int append_blocks64(const AppendParams& p);
-// Query rows one attention unit takes at most, for a head dim; calls with more
-// rows are split into tiles of this many rows.
+// Query rows one single-wave attention unit takes at most, for a head dim.
 int max_rows_for_head_dim(int head_dim);
+// Query rows per unit for a call with `rows` rows per kv head: all of them when
+// one wave takes them; else a multi-wave workgroup's tile (16-bit pools) or a
+// single wave's (fp32 and E4M3 pools).
+int tile_rows_for_call(int dtype, int head_dim, int rows);
 
 }  // namespace pa

@@ -261,7 +261,7 @@ void make_plan(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, int rows, 
   units.clear();
   tail.clear();
   p->merges.clear();
-  const int tr = std::min(rows, rows_limit(p));
+  const int tr = pa::tile_rows_for_call(p->dtype, p->head_dim, rows);
   int64_t slots = 0;
   for (int i = 0; i < n_seq; ++i) {
     const int parts = p->parts[i];
@@ -592,7 +592,7 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   ak.group = group;
   ak.k_draft = k_draft;
   ak.rows = rows;
-  ak.tile_rows = std::min(rows, rows_limit(p));
+  ak.tile_rows = pa::tile_rows_for_call(p->dtype, p->head_dim, rows);
   ak.head_dim = p->head_dim;
   ak.scale_log2 = scale * 1.4426950408889634f;
   ak.stream_kv = p->bp.num_shared() == 0 ? 1 : 0;
