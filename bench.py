@@ -421,7 +421,8 @@ def main():
         attn_ms = kern[0][0] / kern[0][1]
         # a fused launch also reads the new rows and writes them into the pool
         launch_b = dec_b + (app_b if fused else 0)
-        kname = "attn_append_kernel" if fused else "attn_kernel"
+        multi_wave = not one_tile and cd in ("f16", "bf16")  # LDS-shared row tiles
+        kname = "attn_append_kernel" if fused else ("tile_kernel" if multi_wave else "attn_kernel")
         achieved = launch_b / (attn_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_GBS, 4), "traffic": measured_traffic(wkey, kname),
