@@ -111,6 +111,39 @@ int pa_destroy_pool(pa_pool* pool);
  * device table rows are written by the next device call. */
 int pa_alloc_blocks(pa_pool* pool, int seq_id, int parent_seq, int shared_tokens);
 
+/* Prefix cache.  A later prompt that starts with the same tokens as an earlier
+ * one can reuse that prompt's cached K/V instead of recomputing it; the reuse
+ * runs from the first token up to the first token that differs, never past it
+ * (ranksignal.fr post 218, "Mettre en cache"; blocks shared copy-on-write:
+ * "PagedAttention, décodage spéculatif, MoE et Blackwell", section 1).  Here
+ * the unit of reuse is a whole 16-token block: block j is reused when tokens
+ * [0, 16 (j + 1)) all agree.  tokens are host int32 token ids, caller-defined;
+ * the library trusts that they name the rows the sequence holds.  Host-side
+ * only: device tables are written by the next device call.
+ *
+ * pa_prefix_insert: register the full blocks among the first
+ *   min(n_tokens, length) tokens of live sequence seq_id that are not
+ *   registered yet; each one gains a reference held by the cache (so it
+ *   outlives the sequence).  *n_new (may be NULL) = blocks newly registered.
+ * pa_prefix_match: *n_matched = tokens (a multiple of 16) at the start of
+ *   tokens[0, n_tokens) held by registered blocks.  Changes nothing.
+ * pa_alloc_from_prefix: start sequence seq_id (in range, not live) sharing the
+ *   matched blocks (one more reference each), with length *n_matched (may be
+ *   NULL); the caller appends the rest of the prompt.  A later write into a
+ *   reused block is copied first, as for any shared block.
+ * pa_prefix_evict: drop up to max_entries entries, one at a time, always one
+ *   that no other entry extends, least recently used first (inserts and
+ *   reuses mark the entries they pass), ties to the oldest; blocks left
+ *   unreferenced go to the back of the free list.  *n_evicted may be NULL.
+ *   The library never evicts by itself: on PA_ERR_NOMEM the caller may evict
+ *   and retry.
+ * pa_prefix_entries: *n = registered blocks. */
+int pa_prefix_insert(pa_pool* pool, int seq_id, const int32_t* tokens, int n_tokens, int* n_new);
+int pa_prefix_match(const pa_pool* pool, const int32_t* tokens, int n_tokens, int* n_matched);
+int pa_alloc_from_prefix(pa_pool* pool, int seq_id, const int32_t* tokens, int n_tokens, int* n_matched);
+int pa_prefix_evict(pa_pool* pool, int max_entries, int* n_evicted);
+int pa_prefix_entries(const pa_pool* pool, int* n);
+
 /* Scales of a PA_FP8_E4M3 pool, one per kv head: host float arrays
  * [num_kv_heads], finite and > 0 (default 1.0).  Codes already stored are
  * not rewritten: set the scales before the first append.  Synchronous.

@@ -45,7 +45,8 @@ class PrefixCacheModel:
         """Tokens (a multiple of 16) at the start of ``tokens`` held by registered blocks."""
         t = tuple(int(x) for x in tokens)
         m = 0
-        while len(t) >= BLOCK * (m + 1) and t[: BLOCK * (m + 1)] in self.entries:
+        # (at most one sequence's table of blocks)
+        while m < self.pool.max_blocks and len(t) >= BLOCK * (m + 1) and t[: BLOCK * (m + 1)] in self.entries:
             m += 1
         return BLOCK * m
 

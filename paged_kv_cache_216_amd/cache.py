@@ -106,6 +106,38 @@ class PagedKVCache:
     def alloc(self, seq: int, parent: int = -1, shared_tokens: int = 0) -> None:
         abi.check(self.lib.pa_alloc_blocks(self.handle, seq, parent, shared_tokens))
 
+    # ---- prefix cache ------------------------------------------------------
+    def prefix_insert(self, seq: int, tokens) -> int:
+        """Register the full blocks of ``seq`` named by ``tokens``; returns the
+        number of newly registered blocks."""
+        ids, n = abi.i32_array(tokens)
+        out = ctypes.c_int()
+        abi.check(self.lib.pa_prefix_insert(self.handle, seq, ids, n, ctypes.byref(out)))
+        return out.value
+
+    def prefix_match(self, tokens) -> int:
+        ids, n = abi.i32_array(tokens)
+        out = ctypes.c_int()
+        abi.check(self.lib.pa_prefix_match(self.handle, ids, n, ctypes.byref(out)))
+        return out.value
+
+    def alloc_from_prefix(self, seq: int, tokens) -> int:
+        """Start ``seq`` on the cached leading blocks of ``tokens``; returns its length."""
+        ids, n = abi.i32_array(tokens)
+        out = ctypes.c_int()
+        abi.check(self.lib.pa_alloc_from_prefix(self.handle, seq, ids, n, ctypes.byref(out)))
+        return out.value
+
+    def prefix_evict(self, max_entries: int) -> int:
+        out = ctypes.c_int()
+        abi.check(self.lib.pa_prefix_evict(self.handle, max_entries, ctypes.byref(out)))
+        return out.value
+
+    def prefix_entries(self) -> int:
+        out = ctypes.c_int()
+        abi.check(self.lib.pa_prefix_entries(self.handle, ctypes.byref(out)))
+        return out.value
+
     def append(self, seq_ids: Sequence[int], n_tok, k_new: Optional[torch.Tensor],
                v_new: Optional[torch.Tensor], stream=None) -> None:
         """k_new / v_new: [sum(n_tok), Hkv, D] device tensors in the pool dtype."""

@@ -41,6 +41,12 @@ int BlockPool::init(int num_blocks, int max_seqs, int max_blocks_per_seq,
   num_shared_ = 0;
   rc_delta_.assign(num_blocks, 0);
   touched_.clear();
+  pentries_.clear();
+  pfree_ids_.clear();
+  pindex_.clear();
+  pleaves_.clear();
+  pclock_ = 0;
+  porder_ = 0;
   return kOk;
 }
 
@@ -171,6 +177,148 @@ int BlockPool::free_seq(int seq, std::string* err) {
   if (rc != kOk) return rc;
   len_[seq] = -1;
   mark_len(seq);
+  return kOk;
+}
+
+// ---- prefix cache -----------------------------------------------------------
+
+namespace {
+
+uint64_t prefix_key(int32_t parent, const int32_t* tok) {
+  uint64_t h = 1469598103934665603ull;  // FNV-1a, 64 bits
+  auto mix = [&h](uint32_t v) {
+    for (int b = 0; b < 4; ++b) {
+      h ^= (v >> (8 * b)) & 0xFFu;
+      h *= 1099511628211ull;
+    }
+  };
+  mix(static_cast<uint32_t>(parent));
+  for (int i = 0; i < kBlock; ++i) mix(static_cast<uint32_t>(tok[i]));
+  return h;
+}
+
+}  // namespace
+
+int32_t BlockPool::prefix_find(int32_t parent, const int32_t* tok) const {
+  const auto range = pindex_.equal_range(prefix_key(parent, tok));
+  for (auto it = range.first; it != range.second; ++it) {
+    const PrefixEntry& e = pentries_[it->second];
+    if (e.parent == parent && std::equal(tok, tok + kBlock, e.tok)) return it->second;
+  }
+  return -1;
+}
+
+void BlockPool::prefix_touch(int32_t id, uint64_t clock) {
+  PrefixEntry& e = pentries_[id];
+  if (e.children == 0) {
+    pleaves_.erase({e.last, e.order, id});
+    pleaves_.insert({clock, e.order, id});
+  }
+  e.last = clock;
+}
+
+int BlockPool::prefix_insert(int seq, const int32_t* tokens, int n_tokens, int* n_new, std::string* err) {
+  if (!live(seq)) return fail(err, kInvalid, "prefix insert from a sequence that is not live");
+  if (n_tokens < 0 || (n_tokens > 0 && !tokens)) return fail(err, kInvalid, "bad token array");
+  const int nb = std::min(n_tokens, len_[seq]) / kBlock;
+  const std::vector<int32_t>& tab = tables_[seq];
+  const uint64_t clock = ++pclock_;
+  int added = 0;
+  int32_t parent = -1;
+  for (int j = 0; j < nb; ++j) {
+    const int32_t* tok = tokens + j * kBlock;
+    int32_t id = prefix_find(parent, tok);
+    if (id < 0) {
+      if (pfree_ids_.empty()) {
+        id = static_cast<int32_t>(pentries_.size());
+        pentries_.emplace_back();
+      } else {
+        id = pfree_ids_.back();
+        pfree_ids_.pop_back();
+      }
+      PrefixEntry& e = pentries_[id];
+      e.parent = parent;
+      e.block = tab[j];
+      e.children = 0;
+      e.last = clock;
+      e.order = porder_++;
+      std::copy(tok, tok + kBlock, e.tok);
+      pindex_.insert({prefix_key(parent, tok), id});
+      pleaves_.insert({clock, e.order, id});
+      if (parent >= 0) {
+        PrefixEntry& pe = pentries_[parent];
+        if (pe.children++ == 0) pleaves_.erase({pe.last, pe.order, parent});
+      }
+      if (++rc_[e.block] == 2) ++num_shared_;
+      ++added;
+    } else {
+      prefix_touch(id, clock);
+    }
+    parent = id;
+  }
+  if (n_new) *n_new = added;
+  return kOk;
+}
+
+int BlockPool::prefix_match(const int32_t* tokens, int n_tokens) const {
+  if (n_tokens <= 0 || !tokens) return 0;
+  int m = 0;
+  int32_t parent = -1;
+  while ((m + 1) * kBlock <= n_tokens && m < max_blocks_) {
+    const int32_t id = prefix_find(parent, tokens + m * kBlock);
+    if (id < 0) break;
+    parent = id;
+    ++m;
+  }
+  return m * kBlock;
+}
+
+int BlockPool::alloc_from_prefix(int seq, const int32_t* tokens, int n_tokens, int* n_matched,
+                                 std::string* err) {
+  if (seq < 0 || seq >= max_seqs_) return fail(err, kInvalid, "seq id out of range");
+  if (len_[seq] >= 0) return fail(err, kInvalid, "seq id already live");
+  if (n_tokens < 0 || (n_tokens > 0 && !tokens)) return fail(err, kInvalid, "bad token array");
+  const int m = prefix_match(tokens, n_tokens);
+  const uint64_t clock = ++pclock_;
+  tables_[seq].clear();
+  int32_t parent = -1;
+  for (int j = 0; j < m / kBlock; ++j) {
+    const int32_t id = prefix_find(parent, tokens + j * kBlock);
+    prefix_touch(id, clock);
+    const int32_t b = pentries_[id].block;
+    tables_[seq].push_back(b);
+    if (++rc_[b] == 2) ++num_shared_;
+    mark_entry(seq, j);
+    parent = id;
+  }
+  len_[seq] = m;
+  mark_len(seq);
+  if (n_matched) *n_matched = m;
+  return kOk;
+}
+
+int BlockPool::prefix_evict(int max_entries, int* n_evicted, std::string* err) {
+  if (max_entries < 0) return fail(err, kInvalid, "max_entries < 0");
+  int done = 0;
+  while (done < max_entries && !pleaves_.empty()) {
+    const int32_t id = std::get<2>(*pleaves_.begin());
+    pleaves_.erase(pleaves_.begin());
+    PrefixEntry& e = pentries_[id];
+    const auto range = pindex_.equal_range(prefix_key(e.parent, e.tok));
+    for (auto it = range.first; it != range.second; ++it)
+      if (it->second == id) {
+        pindex_.erase(it);
+        break;
+      }
+    release(e.block);
+    if (e.parent >= 0) {
+      PrefixEntry& pe = pentries_[e.parent];
+      if (--pe.children == 0) pleaves_.insert({pe.last, pe.order, e.parent});
+    }
+    pfree_ids_.push_back(id);
+    ++done;
+  }
+  if (n_evicted) *n_evicted = done;
   return kOk;
 }
 

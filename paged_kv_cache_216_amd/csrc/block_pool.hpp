@@ -17,7 +17,10 @@
 
 #include <cstdint>
 #include <deque>
+#include <set>
 #include <string>
+#include <tuple>
+#include <unordered_map>
 #include <vector>
 
 namespace pa {
@@ -44,6 +47,18 @@ class BlockPool {
              std::vector<CowCopy>* cows, std::string* err);
   int truncate(int seq, int new_len, std::string* err);
   int free_seq(int seq, std::string* err);
+
+  // Prefix cache: whole blocks registered under the token ids of the prompt up
+  // to the end of the block (a chain of (parent entry, 16 tokens) keys), each
+  // holding one reference on its block.  Reuse runs from the first block to the
+  // first block whose tokens differ ("Mettre en cache" on the ranksignal.fr
+  // page).  Inserts and reuses tick a clock; eviction drops entries no other
+  // entry extends, least recently used first, ties to the oldest entry.
+  int prefix_insert(int seq, const int32_t* tokens, int n_tokens, int* n_new, std::string* err);
+  int prefix_match(const int32_t* tokens, int n_tokens) const;  // matched tokens
+  int alloc_from_prefix(int seq, const int32_t* tokens, int n_tokens, int* n_matched, std::string* err);
+  int prefix_evict(int max_entries, int* n_evicted, std::string* err);
+  int prefix_entries() const { return static_cast<int>(pindex_.size()); }
 
   bool live(int seq) const { return seq >= 0 && seq < max_seqs_ && len_[seq] >= 0; }
   int length(int seq) const { return len_[seq]; }
@@ -99,6 +114,23 @@ class BlockPool {
   std::vector<int32_t> dirty_entry_list_, dirty_len_list_;
   std::vector<int32_t> rc_delta_, touched_;
   int num_shared_ = 0;
+
+  struct PrefixEntry {
+    int32_t parent;    // entry of the previous block, -1 for a prompt's first block
+    int32_t block;
+    int32_t children;  // entries that extend this one
+    uint64_t last;     // clock of the last insert / reuse through it
+    int64_t order;     // registration order
+    int32_t tok[kBlock];
+  };
+  int32_t prefix_find(int32_t parent, const int32_t* tok) const;
+  void prefix_touch(int32_t id, uint64_t clock);
+  std::vector<PrefixEntry> pentries_;
+  std::vector<int32_t> pfree_ids_;                      // reusable entry slots
+  std::unordered_multimap<uint64_t, int32_t> pindex_;   // key hash -> entry
+  std::set<std::tuple<uint64_t, int64_t, int32_t>> pleaves_;  // (last, order, entry) of leaves
+  uint64_t pclock_ = 0;
+  int64_t porder_ = 0;
 };
 
 }  // namespace pa

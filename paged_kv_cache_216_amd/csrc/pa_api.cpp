@@ -750,6 +750,40 @@ int pa_alloc_blocks(pa_pool* p, int seq_id, int parent_seq, int shared_tokens) {
   return rc == pa::kOk ? PA_OK : set_err(rc, err);
 }
 
+int pa_prefix_insert(pa_pool* p, int seq_id, const int32_t* tokens, int n_tokens, int* n_new) {
+  if (!p) return set_err(PA_ERR_INVALID, "pool is NULL");
+  std::string err;
+  int rc = p->bp.prefix_insert(seq_id, tokens, n_tokens, n_new, &err);
+  return rc == pa::kOk ? PA_OK : set_err(rc, err);
+}
+
+int pa_prefix_match(const pa_pool* p, const int32_t* tokens, int n_tokens, int* n_matched) {
+  if (!p || !n_matched) return set_err(PA_ERR_INVALID, "NULL argument");
+  if (n_tokens < 0 || (n_tokens > 0 && !tokens)) return set_err(PA_ERR_INVALID, "bad token array");
+  *n_matched = p->bp.prefix_match(tokens, n_tokens);
+  return PA_OK;
+}
+
+int pa_alloc_from_prefix(pa_pool* p, int seq_id, const int32_t* tokens, int n_tokens, int* n_matched) {
+  if (!p) return set_err(PA_ERR_INVALID, "pool is NULL");
+  std::string err;
+  int rc = p->bp.alloc_from_prefix(seq_id, tokens, n_tokens, n_matched, &err);
+  return rc == pa::kOk ? PA_OK : set_err(rc, err);
+}
+
+int pa_prefix_evict(pa_pool* p, int max_entries, int* n_evicted) {
+  if (!p) return set_err(PA_ERR_INVALID, "pool is NULL");
+  std::string err;
+  int rc = p->bp.prefix_evict(max_entries, n_evicted, &err);
+  return rc == pa::kOk ? PA_OK : set_err(rc, err);
+}
+
+int pa_prefix_entries(const pa_pool* p, int* n) {
+  if (!p || !n) return set_err(PA_ERR_INVALID, "NULL argument");
+  *n = p->bp.prefix_entries();
+  return PA_OK;
+}
+
 int pa_set_kv_scales(pa_pool* p, const float* k_scale, const float* v_scale) {
   if (!p || !k_scale || !v_scale) return set_err(PA_ERR_INVALID, "NULL argument");
   if (p->dtype != PA_FP8_E4M3) return set_err(PA_ERR_STATE, "scales belong to PA_FP8_E4M3 pools");
