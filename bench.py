@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="highbatch",
                     choices=["highbatch", "gqa70b", "long", "verify", "tiny", "prefill"])
+    ap.add_argument("--swap", action="store_true",
+                    help="measure block swap instead: every sequence of the workload out to pinned host "
+                         "memory and back in, per step")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--partition-tokens", type=int, default=0,
                     help="split-KV partition length; 0: the workload's (or the library's) choice; -1: no split")
@@ -320,6 +323,56 @@ def measured_traffic(workload: str, kernel: str):
     return None
 
 
+PCIE_GBS = 64.0  # PCIe 5.0 x16, one direction, the MI355X host link
+
+
+def run_swap(args, w):
+    """Block swap to pinned host memory: a step swaps every sequence of one
+    pool out (pa_swap_out, device -> host) and back in (pa_swap_in, host ->
+    device).  Reported in GB/s of K/V bytes moved over the host link."""
+    import torch
+    rep = Replica(w, 0)
+    c = rep.cache
+    lens = [int(n) for n in w.lengths + w.prefix_len]
+    imgs = []
+    for n in lens:
+        nb = c.swap_bytes(n)
+        imgs.append((torch.empty(nb, dtype=torch.uint8, pin_memory=True),
+                     torch.empty(nb, dtype=torch.uint8, pin_memory=True)))
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for s, (ki, vi) in enumerate(imgs):
+            c.swap_out(s, ki, vi, stream)
+        for s, (ki, vi) in enumerate(imgs):
+            c.swap_in(s, lens[s], ki, vi, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    moved = 2 * sum(2 * c.swap_bytes(n) for n in lens)  # K and V images, out and in
+    gbs = moved / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "block swap GB/s (device <-> pinned host, K/V images out and back in)", "value": round(gbs, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: {describe(w)}; step = every sequence swapped out, then back in",
+                   "bytes_per_step": moved, "sequences": len(lens)},
+        "roofline": {"bound": "pcie", "achieved": round(gbs, 2), "peak": PCIE_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PCIE_GBS, 4), "traffic": None,
+                     "note": "the out and in copies run one after the other, each bound by one direction"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -334,6 +387,8 @@ def main():
     assert torch.cuda.is_available(), "bench needs a GPU"
     torch.cuda.set_device(0)
     w = make_workload(args.workload)
+    if args.swap:
+        return run_swap(args, w)
     pt = args.partition_tokens if args.partition_tokens else (w.partition_tokens or 0)
     cd, scales, wkey = w.dtype, None, w.name
     if args.kv_cache == "fp8":

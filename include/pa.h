@@ -111,6 +111,33 @@ int pa_destroy_pool(pa_pool* pool);
  * device table rows are written by the next device call. */
 int pa_alloc_blocks(pa_pool* pool, int seq_id, int parent_seq, int shared_tokens);
 
+/* Block swap to host memory.  When GPU memory runs short, a KV cache can move
+ * blocks to slower tiers and bring them back when needed; host RAM is the
+ * tier after GPU memory (ranksignal.fr post 218, "Mettre en cache", tiers
+ * G1 and G2).  The host images are caller-owned pinned host memory
+ * (hipHostMalloc, or a pinned torch tensor), one for K and one for V, each
+ * [ceil(length / 16)][num_kv_heads x 16 x head_dim elements]: every block in
+ * the pool's own layout, in logical order.  pa_swap_bytes gives the bytes of
+ * one image for n_tokens tokens.  The copies run on `stream` (one kernel
+ * reading or writing the host images over the bus); the host images must stay
+ * valid, and work on other streams must wait for `stream`, until they finish.
+ *
+ * pa_swap_out: copy live sequence seq_id's blocks into the images, then end
+ *   the sequence as pa_free_seq does (its blocks lose one reference; shared
+ *   blocks stay with their other holders).  *length (may be NULL) = its
+ *   length, which pa_swap_in takes back.
+ * pa_swap_in: start seq_id (in range, not live) with `length` rows taken from
+ *   the images: the blocks are popped from the free list as an append of
+ *   `length` rows would pop them (PA_ERR_NOMEM, changing nothing, if there are
+ *   too few); slots past `length` in the last block are not written.
+ * Errors: PA_ERR_INVALID for bad ids, short or unpinned buffers;
+ * PA_ERR_STATE for host-only pools. */
+int pa_swap_bytes(const pa_pool* pool, int n_tokens, size_t* bytes);
+int pa_swap_out(pa_pool* pool, int seq_id, void* k_host, void* v_host, size_t bytes, int* length,
+                void* stream);
+int pa_swap_in(pa_pool* pool, int seq_id, int length, const void* k_host, const void* v_host, size_t bytes,
+               void* stream);
+
 /* Prefix cache.  A later prompt that starts with the same tokens as an earlier
  * one can reuse that prompt's cached K/V instead of recomputing it; the reuse
  * runs from the first token up to the first token that differs, never past it

@@ -232,6 +232,42 @@ class PoolModel:
         del self.tables[seq]
         del self.lens[seq]
 
+    # ---- swap to host memory -------------------------------------------------
+    # A KV cache short of GPU memory can move a sequence's blocks to host RAM
+    # and bring them back later ([P4] "Mettre en cache", tiers G1 / G2).  Here
+    # swapping out keeps the sequence's rows (stored codes, bit for bit) and
+    # ends it; swapping in starts a sequence and writes those rows into blocks
+    # taken as an append of that many rows would take them.
+    def swap_out(self, seq: int):
+        """Rows of ``seq`` as stored ([n, Hkv, D] bit patterns); ``seq`` ends."""
+        if not self.live(seq):
+            raise InvalidError(f"seq {seq} does not exist")
+        k, v = self.gather(seq) if self.track_data else (None, None)
+        n = self.lens[seq]
+        self.free_seq(seq)
+        return n, k, v
+
+    def swap_in(self, seq: int, n: int, k_bits=None, v_bits=None) -> None:
+        """Start ``seq`` with ``n`` rows given as stored bit patterns."""
+        self._check_seq_id(seq)
+        if self.live(seq):
+            raise InvalidError(f"seq {seq} already exists")
+        if n < 0:
+            raise InvalidError("length < 0")
+        if (n + BLOCK - 1) // BLOCK > self.max_blocks:
+            raise InvalidError("longer than a block table")
+        if (n + BLOCK - 1) // BLOCK > len(self.free):
+            raise NoMemError("pool exhausted")
+        self.tables[seq] = []
+        self.lens[seq] = 0
+        for t in range(n):
+            if t % BLOCK == 0:
+                self.tables[seq].append(self._pop())
+            if self.track_data:
+                layout.write_row(self.kpool, self.vpool, self.tables[seq][-1], t % BLOCK, k_bits[t], v_bits[t],
+                                 self.dtype)
+            self.lens[seq] = t + 1
+
     # ---- views for comparison -----------------------------------------------
     def gather(self, seq: int):
         """Logical K, V rows of ``seq`` ([n, Hkv, D] bit patterns), read through

@@ -33,6 +33,9 @@ SIGNATURES = {
                           c_void_p, c_size_t, c_void_p]),
     "pa_verify": (c_int, [c_void_p, c_i32p, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p,
                           c_int, c_void_p, c_size_t, c_void_p]),
+    "pa_swap_bytes": (c_int, [c_void_p, c_int, ctypes.POINTER(c_size_t)]),
+    "pa_swap_out": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_size_t, c_intp, c_void_p]),
+    "pa_swap_in": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
     "pa_prefix_insert": (c_int, [c_void_p, c_int, c_i32p, c_int, c_intp]),
     "pa_prefix_match": (c_int, [c_void_p, c_i32p, c_int, c_intp]),
     "pa_alloc_from_prefix": (c_int, [c_void_p, c_int, c_i32p, c_int, c_intp]),

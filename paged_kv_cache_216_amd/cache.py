@@ -106,6 +106,25 @@ class PagedKVCache:
     def alloc(self, seq: int, parent: int = -1, shared_tokens: int = 0) -> None:
         abi.check(self.lib.pa_alloc_blocks(self.handle, seq, parent, shared_tokens))
 
+    # ---- swap to host ------------------------------------------------------
+    def swap_bytes(self, n_tokens: int) -> int:
+        out = ctypes.c_size_t()
+        abi.check(self.lib.pa_swap_bytes(self.handle, n_tokens, ctypes.byref(out)))
+        return out.value
+
+    def swap_out(self, seq: int, k_host: torch.Tensor, v_host: torch.Tensor, stream=None) -> int:
+        """Copy ``seq`` into pinned host tensors and end it; returns its length."""
+        n = ctypes.c_int()
+        nbytes = min(k_host.numel() * k_host.element_size(), v_host.numel() * v_host.element_size())
+        abi.check(self.lib.pa_swap_out(self.handle, seq, _ptr(k_host), _ptr(v_host), nbytes, ctypes.byref(n),
+                                       _stream(stream)))
+        return n.value
+
+    def swap_in(self, seq: int, length: int, k_host: torch.Tensor, v_host: torch.Tensor, stream=None) -> None:
+        nbytes = min(k_host.numel() * k_host.element_size(), v_host.numel() * v_host.element_size())
+        abi.check(self.lib.pa_swap_in(self.handle, seq, length, _ptr(k_host), _ptr(v_host), nbytes,
+                                      _stream(stream)))
+
     # ---- prefix cache ------------------------------------------------------
     def prefix_insert(self, seq: int, tokens) -> int:
         """Register the full blocks of ``seq`` named by ``tokens``; returns the

@@ -23,6 +23,7 @@
 
 #include "block_pool.hpp"
 #include "kernels.hpp"
+#include "swap.hpp"
 
 namespace {
 
@@ -748,6 +749,113 @@ int pa_alloc_blocks(pa_pool* p, int seq_id, int parent_seq, int shared_tokens) {
   std::string err;
   int rc = p->bp.alloc(seq_id, parent_seq, shared_tokens, &err);
   return rc == pa::kOk ? PA_OK : set_err(rc, err);
+}
+
+int pa_swap_bytes(const pa_pool* p, int n_tokens, size_t* bytes) {
+  if (!p || !bytes) return set_err(PA_ERR_INVALID, "NULL argument");
+  if (n_tokens < 0) return set_err(PA_ERR_INVALID, "n_tokens < 0");
+  const size_t blocks = (static_cast<size_t>(n_tokens) + 15) / 16;
+  *bytes = blocks * p->hkv * 16 * p->head_dim * p->esize;
+  return PA_OK;
+}
+
+namespace {
+
+// Device-visible address of a pinned host buffer.
+int host_dev_ptr(const void* host, char** out) {
+  void* d = nullptr;
+  hipError_t e = hipHostGetDevicePointer(&d, const_cast<void*>(host), 0);
+  if (e != hipSuccess || !d) {
+    (void)hipGetLastError();
+    return set_err(PA_ERR_INVALID, "host buffer is not pinned host memory");
+  }
+  *out = static_cast<char*>(d);
+  return PA_OK;
+}
+
+// Copy the blocks of `table` between the pool and the host images on `stream`.
+int swap_blocks(pa_pool* p, const std::vector<int32_t>& table, char* k_host, char* v_host, int last_rows,
+                bool to_host, hipStream_t stream) {
+  if (table.empty()) return PA_OK;
+  Stage* st = nullptr;
+  int rc = acquire_stage(p, table.size(), &st);
+  if (rc != PA_OK) return rc;
+  std::memcpy(st->host, table.data(), table.size() * sizeof(int32_t));
+  pa::SwapParams sp{};
+  sp.k_pool = static_cast<char*>(p->k_pool);
+  sp.v_pool = static_cast<char*>(p->v_pool);
+  sp.k_host = k_host;
+  sp.v_host = v_host;
+  sp.blocks = st->dev;
+  sp.n_blocks = static_cast<int>(table.size());
+  sp.block_bytes = p->hkv * 16 * p->head_dim * p->esize;
+  sp.line_bytes = 16 * p->esize;
+  sp.elem_bytes = p->esize;
+  sp.last_rows = last_rows;
+  sp.to_host = to_host ? 1 : 0;
+  hipError_t e = pa::launch_swap(sp, stream);
+  if (e != hipSuccess) return hip_err(e, "swap kernel");
+  return release_stage(st, stream);
+}
+
+}  // namespace
+
+int pa_swap_out(pa_pool* p, int seq_id, void* k_host, void* v_host, size_t bytes, int* length, void* stream_v) {
+  if (!p) return set_err(PA_ERR_INVALID, "pool is NULL");
+  if (p->host_only) return set_err(PA_ERR_STATE, "host-only pool has no device memory");
+  if (!p->bp.live(seq_id)) return set_err(PA_ERR_INVALID, "swap out of a sequence that is not live");
+  const int n = p->bp.length(seq_id);
+  size_t need = 0;
+  pa_swap_bytes(p, n, &need);
+  if (bytes < need) return set_err(PA_ERR_INVALID, "host buffers too small (see pa_swap_bytes)");
+  char *kd = nullptr, *vd = nullptr;
+  if (need > 0) {
+    int rc = host_dev_ptr(k_host, &kd);
+    if (rc == PA_OK) rc = host_dev_ptr(v_host, &vd);
+    if (rc != PA_OK) return rc;
+  }
+  hipStream_t stream = static_cast<hipStream_t>(stream_v);
+  const std::vector<int32_t> table = p->bp.table(seq_id);
+  int rc = swap_blocks(p, table, kd, vd, 16, true, stream);
+  if (rc != PA_OK) return rc;
+  std::string err;
+  rc = p->bp.free_seq(seq_id, &err);
+  if (rc != pa::kOk) return set_err(rc, err);
+  if (length) *length = n;
+  return PA_OK;
+}
+
+int pa_swap_in(pa_pool* p, int seq_id, int length, const void* k_host, const void* v_host, size_t bytes,
+               void* stream_v) {
+  if (!p) return set_err(PA_ERR_INVALID, "pool is NULL");
+  if (p->host_only) return set_err(PA_ERR_STATE, "host-only pool has no device memory");
+  if (length < 0) return set_err(PA_ERR_INVALID, "length < 0");
+  size_t need = 0;
+  pa_swap_bytes(p, length, &need);
+  if (bytes < need) return set_err(PA_ERR_INVALID, "host buffers too small (see pa_swap_bytes)");
+  char *kd = nullptr, *vd = nullptr;
+  if (need > 0) {
+    int rc = host_dev_ptr(k_host, &kd);
+    if (rc == PA_OK) rc = host_dev_ptr(v_host, &vd);
+    if (rc != PA_OK) return rc;
+  }
+  std::string err;
+  int rc = p->bp.alloc(seq_id, -1, 0, &err);
+  if (rc != pa::kOk) return set_err(rc, err);
+  // the blocks are taken exactly as an append of `length` rows would take them
+  p->slots.clear();
+  p->cows.clear();
+  rc = p->bp.append(&seq_id, 1, &length, &p->slots, &p->cows, &err);
+  if (rc != pa::kOk) {
+    std::string ignore;
+    p->bp.free_seq(seq_id, &ignore);
+    return set_err(rc, err);
+  }
+  hipStream_t stream = static_cast<hipStream_t>(stream_v);
+  rc = flush_dirty(p, stream);
+  if (rc != PA_OK) return rc;
+  const int last = length % 16 == 0 ? 16 : length % 16;
+  return swap_blocks(p, p->bp.table(seq_id), kd, vd, last, false, stream);
 }
 
 int pa_prefix_insert(pa_pool* p, int seq_id, const int32_t* tokens, int n_tokens, int* n_new) {
