@@ -217,7 +217,19 @@ int pa_append_kv(pa_pool* pool, const int32_t* seq_ids, int n_seq, const int32_t
  * cache of a common prefix: ranksignal.fr post 218, "Mettre en cache").
  * Needs the split (a workspace) and a 16-bit dtype.  Results equal the
  * per-sequence computation up to floating-point summation order.
- * Softmax and accumulation are fp32; out is rounded to dtype (nearest even). */
+ * Softmax and accumulation are fp32; out is rounded to dtype (nearest even).
+ * Graph capture: engines replay a recorded launch sequence instead of
+ * launching kernel by kernel ("CUDA Graphs, modèles de raisonnement et service
+ * désagrégé", section 1).  A pa_decode / pa_verify call can be captured into
+ * a HIP graph on `stream` when it runs unsplit (workspace NULL), the same call
+ * (same sequences, num_q_heads, k_draft) has run once before so that its work
+ * plan is on the device, and the device tables are current (pa_sync_tables).
+ * Each replay then reads the lengths and block tables current at replay time,
+ * so appends made eagerly between replays are seen.  The pool holds one work
+ * plan: an attention call with other sequences between the capture and a
+ * replay invalidates the graph.  Calls that append (pa_append_kv,
+ * pa_append_attend) pass their rows and slots as launch arguments and cannot
+ * be replayed. */
 int pa_decode(pa_pool* pool, const int32_t* seq_ids, int n_seq, int num_q_heads, float scale,
               const void* q, void* out, float* lse, int partition_tokens, void* workspace,
               size_t ws_bytes, void* stream);
