@@ -467,10 +467,9 @@ def main():
     if prefill:
         value = flops / (ms_step * 1e-3) / 1e12
     # 8-bit pools take the append and the attention as two launches
-    # 8-bit pools and calls of several row tiles take the append and the
-    # attention as two launches
+    # calls of several row tiles take the append and the attention as two launches
     one_tile = (w.num_q_heads // w.num_kv_heads) * w.k_draft <= (64 if w.head_dim <= 128 else 32)
-    fused = bool(reps[0].t_new) and not args.separate and cd != "fp8" and one_tile
+    fused = bool(reps[0].t_new) and not args.separate and one_tile
     roof = None
     if kern[0][1]:
         attn_ms = kern[0][0] / kern[0][1]

@@ -72,8 +72,8 @@ typedef enum {
  * to float32, clamped to [-448, 448] and rounded to the nearest code, ties to
  * the even code; the attention uses decode(code) * scale[h], in fp32.  An
  * 8-bit cache halves the bytes a decode step reads while the softmax stays at
- * full precision (ranksignal.fr post 218, "Quantifier").  The 8-bit pools take
- * neither the single-launch append + attention nor the shared-prefix pass. */
+ * full precision (ranksignal.fr post 218, "Quantifier").  The 8-bit pools do
+ * not take the shared-prefix pass. */
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
 
 /* Create a pool over caller-owned device memory.
@@ -266,7 +266,8 @@ int pa_prefill(pa_pool* pool, const int32_t* seq_ids, int n_seq, int n_new, int 
  * the two separate calls.  Falls back to two launches (same results) when a
  * write needs a copy-on-write copy first, when earlier table changes are still
  * pending, when (num_q_heads / num_kv_heads) * n_new is more than one unit's
- * rows (see pa_verify), or for PA_F32 and PA_FP8_E4M3 pools.
+ * rows (see pa_verify), or for PA_F32 pools.  With PA_FP8_E4M3 pools the
+ * attention takes the new rows as the codes the append stores, decoded. 
  *   seq_ids  host int32 [n_seq]; live and distinct
  *   k_new, v_new  device [n_seq * n_new][num_kv_heads][head_dim], rows of
  *            sequence i at i * n_new .. i * n_new + n_new - 1

@@ -437,6 +437,15 @@ __device__ inline u32x2 fp8x4_to_bf16(uint32_t w) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// The bf16 bits of what an E4M3 pool stores for the bf16 value `h` (bits)
+// at reciprocal scale `inv`: the append's rounding (float32 product, clamp,
+// nearest even code), decoded back.
+__device__ inline uint32_t fp8_requant_bf16(uint32_t h, float inv) {
+  const float x = fminf(fmaxf(__uint_as_float(h << 16) * inv, -448.f), 448.f);
+  const uint32_t code = __builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false) & 0xFFu;
+  return __float_as_uint(__builtin_amdgcn_cvt_f32_fp8(code, 0)) >> 16;
+}
+
 template <bool NTL>
 __device__ inline uint32_t page_load4(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, NTL ? 2 : 0));
@@ -452,7 +461,7 @@ __device__ inline uint32_t page_load4(__amdgpu_buffer_rsrc_t r, int byte_off) {
 // workgroup's), so the barriers line up.
 template <typename T, int D, int NT, bool NTL, bool FUSED, bool PREFIX = false, bool Q8 = false, int W = 1>
 __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) {
-  static_assert(!(Q8 && (FUSED || PREFIX)), "E4M3 pools take the plain path");
+  static_assert(!(Q8 && PREFIX), "E4M3 pools take no shared-prefix pass");
   static_assert(W == 1 || !(Q8 || FUSED || PREFIX), "LDS-shared pairs: plain 16-bit path only");
   using Op = typename MfmaOp<T>::type;
   constexpr int KS = D / 32;  // QK k-steps per block
@@ -836,15 +845,30 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       const size_t off1 = (static_cast<size_t>(phys1) * p.hkv + kvh) * page;
       const auto rk0 = page_rsrc(kpool + off0, old0 ? kPageBytes : 0), rv0 = page_rsrc(vpool + off0, old0 ? kPageBytes : 0);
       const auto rk1 = page_rsrc(kpool + off1, old1 ? kPageBytes : 0), rv1 = page_rsrc(vpool + off1, old1 ? kPageBytes : 0);
+      if constexpr (Q8) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        f.k0[s] = __builtin_bit_cast(Op, page_load16<false>(rk0, ((4 * s + grp) * kBlk + col) * 16));
-        f.k1[s] = __builtin_bit_cast(Op, page_load16<false>(rk1, ((4 * s + grp) * kBlk + col) * 16));
-      }
+        for (int s = 0; s < KS; ++s) {
+          const int o = ((2 * s + (grp >> 1)) * kBlk + col) * 16 + 8 * (grp & 1);
+          f.k0[s] = __builtin_bit_cast(Op, fp8x8_to_bf16(page_load8<false>(rk0, o)));
+          f.k1[s] = __builtin_bit_cast(Op, fp8x8_to_bf16(page_load8<false>(rk1, o)));
+        }
 #pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        f.v0[c] = page_load8<false>(rv0, ((16 * c + col) * kBlk + 4 * grp) * 2);
-        f.v1[c] = page_load8<false>(rv1, ((16 * c + col) * kBlk + 4 * grp) * 2);
+        for (int c = 0; c < DC; ++c) {
+          const int o = (16 * c + col) * kBlk + 4 * grp;
+          f.v0[c] = fp8x4_to_bf16(page_load4<false>(rv0, o));
+          f.v1[c] = fp8x4_to_bf16(page_load4<false>(rv1, o));
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          f.k0[s] = __builtin_bit_cast(Op, page_load16<false>(rk0, ((4 * s + grp) * kBlk + col) * 16));
+          f.k1[s] = __builtin_bit_cast(Op, page_load16<false>(rk1, ((4 * s + grp) * kBlk + col) * 16));
+        }
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          f.v0[c] = page_load8<false>(rv0, ((16 * c + col) * kBlk + 4 * grp) * 2);
+          f.v1[c] = page_load8<false>(rv1, ((16 * c + col) * kBlk + 4 * grp) * 2);
+        }
       }
       // splice in the new rows, one token at a time: the row's loads are all
       // issued before any is used, and the splice is selects only
@@ -861,6 +885,21 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
         for (int s = 0; s < KS; ++s) x[s] = __builtin_bit_cast(Op, *reinterpret_cast<const u32x4*>(kn + row + 32 * s + 8 * grp));
 #pragma unroll
         for (int c = 0; c < DC; ++c) nv[c] = vn[row + 16 * c + col];
+        if constexpr (Q8) {
+          // the values the pool will hold: the append's E4M3 codes, decoded
+          const float ki = p.kv_scale[2 * p.hkv + kvh], vi = p.kv_scale[3 * p.hkv + kvh];
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            const u32x4 w = __builtin_bit_cast(u32x4, x[s]);
+            u32x4 r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              r[e] = fp8_requant_bf16(w[e] & 0xFFFFu, ki) | (fp8_requant_bf16(w[e] >> 16, ki) << 16);
+            x[s] = __builtin_bit_cast(Op, r);
+          }
+#pragma unroll
+          for (int c = 0; c < DC; ++c) nv[c] = static_cast<uint16_t>(fp8_requant_bf16(nv[c], vi));
+        }
         const bool kl = col == t;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -1222,16 +1261,16 @@ void tile_kernel(AttnParams p) {
 // the append work (table / length updates and the scatter of the new rows).
 // (two waves per SIMD for the single-tile 128-dim case: the pool pass needs
 // them to keep enough loads in flight)
-template <typename T, int D, int NT, bool NTL>
+template <typename T, int D, int NT, bool NTL, bool Q8 = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 && D == 128 ? 2 : 1)))
 void attn_append_kernel(AttnParams p, InlineMeta im) {
   const int32_t* meta = p.app.ext ? p.app.ext : im.w;
   const int n_attn = p.n_units * p.hkv;
   if (static_cast<int>(blockIdx.x) >= n_attn) {
-    append_work<static_cast<int>(sizeof(T))>(p.app, meta, blockIdx.x - n_attn, 64);
+    append_work<Q8 ? 1 : static_cast<int>(sizeof(T))>(p.app, meta, blockIdx.x - n_attn, 64);
     return;
   }
-  attn_unit<T, D, NT, NTL, true>(p, meta);
+  attn_unit<T, D, NT, NTL, true, Q8>(p, meta);
 }
 
 // Shared-prefix pass: one workgroup of W waves per (prefix unit, kv head);
@@ -1350,10 +1389,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
 
 template <typename T, int D, int NT, bool NTL, bool Q8>
 void launch_attn_nt(const AttnParams& p, const InlineMeta& m, hipStream_t stream) {
-  if constexpr (!std::is_same_v<T, float> && !Q8) {
+  if constexpr (!std::is_same_v<T, float>) {
     if (p.t_new > 0) {
       const dim3 grid(static_cast<unsigned>(p.n_units) * p.hkv + p.app_blocks);
-      hipLaunchKernelGGL((attn_append_kernel<T, D, NT, NTL>), grid, dim3(64), 0, stream, p, m);
+      hipLaunchKernelGGL((attn_append_kernel<T, D, NT, NTL, Q8>), grid, dim3(64), 0, stream, p, m);
       return;
     }
   }
@@ -1363,8 +1402,8 @@ void launch_attn_nt(const AttnParams& p, const InlineMeta& m, hipStream_t stream
 
 template <typename T, int D, bool NTL, bool Q8>
 hipError_t launch_attn_d(const AttnParams& p, const InlineMeta& m, hipStream_t stream) {
-  // no fused fp32 or E4M3 path
-  if ((std::is_same_v<T, float> || Q8) && p.t_new > 0) return hipErrorInvalidValue;
+  // no fused fp32 path
+  if (std::is_same_v<T, float> && p.t_new > 0) return hipErrorInvalidValue;
   if constexpr (!std::is_same_v<T, float> && !Q8) {
     if (p.tile_rows > max_rows_for_head_dim(D)) {
       if (p.tile_rows != TileShape<D>::kRows || p.t_new > 0) return hipErrorInvalidValue;

@@ -511,8 +511,7 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
     // the new ones, which the attention takes from k_new / v_new).
     // (a call with several row tiles appends first: each tile would splice
     // the new rows again)
-    fused = p->cows.empty() && !table_pending && (p->dtype == PA_F16 || p->dtype == PA_BF16) &&
-            rows <= rows_limit(p);
+    fused = p->cows.empty() && !table_pending && p->dtype != PA_F32 && rows <= rows_limit(p);
     if (!fused) {
       p->bp.take_dirty(&p->dirty);
       rc = launch_append_call(p, app->k_new, app->v_new, stream);
