@@ -405,37 +405,21 @@ __device__ inline void merge_last(const AttnParams& p, const Unit& u, int kvh) {
 }
 
 // 16-bit element types: bf16 or f16
-// E4M3 codes to bf16 (exact: every E4M3 value is a bf16 value).  One
-// conversion per byte: hipcc mis-tracks the second result of the two-code
-// conversion (v_cvt_pk_f32_fp8) once its bits are reused, so it is not used.
-__device__ inline __bf16 fp8_to_bf16(uint32_t w, int byte) {
-  float f = 0.f;
-  switch (byte) {  // the byte select must be an immediate
-    case 0: f = __builtin_amdgcn_cvt_f32_fp8(w, 0); break;
-    case 1: f = __builtin_amdgcn_cvt_f32_fp8(w, 1); break;
-    case 2: f = __builtin_amdgcn_cvt_f32_fp8(w, 2); break;
-    default: f = __builtin_amdgcn_cvt_f32_fp8(w, 3); break;
-  }
-  return static_cast<__bf16>(f);
+// E4M3 codes to bf16 (exact: every E4M3 value, subnormals included, is a
+// bf16 value).  gfx950 converts two codes per instruction: the low or high
+// 16-bit half of a dword (the half select must be an immediate), scale 1.
+__device__ inline uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi) {
+  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false));
 }
 
 __device__ inline bf16x8 fp8x8_to_bf16(u32x2 w) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[i] = fp8_to_bf16(w[0], i);
-    r[4 + i] = fp8_to_bf16(w[1], i);
-  }
-  return r;
+  const u32x4 r = {fp8x2_to_bf16x2(w[0], false), fp8x2_to_bf16x2(w[0], true), fp8x2_to_bf16x2(w[1], false),
+                   fp8x2_to_bf16x2(w[1], true)};
+  return __builtin_bit_cast(bf16x8, r);
 }
 
-__device__ inline u32x2 fp8x4_to_bf16(uint32_t w) {
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  bf16x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = fp8_to_bf16(w, i);
-  return __builtin_bit_cast(u32x2, r);
-}
+__device__ inline u32x2 fp8x4_to_bf16(uint32_t w) { return u32x2{fp8x2_to_bf16x2(w, false), fp8x2_to_bf16x2(w, true)}; }
 
 // The bf16 bits of what an E4M3 pool stores for the bf16 value `h` (bits)
 // at reciprocal scale `inv`: the append's rounding (float32 product, clamp,

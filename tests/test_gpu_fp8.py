@@ -112,7 +112,7 @@ def test_fp8_verify_shared_prefix_copy_on_write(head_dim, g, kd):
 
 
 def test_fp8_append_attend_matches_separate_calls():
-    """pa_append_attend on an 8-bit pool (issued as append, then attention)
+    """pa_append_attend on an 8-bit pool (one launch: append and attention)
     equals the two calls made one after the other, bitwise, and the oracle."""
     w = make_custom(lengths=[15, 16, 31, 200, 513, 1], mode="append_decode", num_q_heads=32, num_kv_heads=8,
                     head_dim=128, dtype="bf16", seed=63)
