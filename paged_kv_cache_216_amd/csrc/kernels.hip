@@ -404,6 +404,10 @@ __device__ inline void merge_last(const AttnParams& p, const Unit& u, int kvh) {
   }
 }
 
+// Largest amount (log2 domain) by which a score may exceed its row's
+// reference maximum before the maximum moves: probabilities stay <= 256.
+constexpr float kMaxSlack = 8.f;
+
 // 16-bit element types: bf16 or f16
 // E4M3 codes to bf16 (exact: every E4M3 value, subnormals included, is a
 // bf16 value).  gfx950 converts two codes per instruction: the low or high
@@ -577,7 +581,13 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
 #pragma unroll
       for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
       mt = wave_max_groups(mt);
-      const float m_new = fmaxf(m_run[nt], mt);
+      // The reference maximum of a row moves only when a score exceeds it by
+      // more than kMaxSlack (log2 units), so probabilities stay <= 2^kMaxSlack:
+      // exact in real arithmetic (acc, l and m stay consistent), no precision
+      // lost (bf16 and fp32 keep their relative precision at that size), and
+      // the accumulator rescale becomes rare.  A first finite score always
+      // sets it (-inf + slack is -inf).
+      const float m_new = (mt > m_run[nt] + kMaxSlack) ? mt : m_run[nt];
       const float m_use = (m_new == kNegInf) ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
       float ps = 0.f;
@@ -589,12 +599,9 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       }
       l_run[nt] = l_run[nt] * alpha + ps;
       m_run[nt] = m_new;
-      // Once the running maxima settle, alpha is exactly 1 on every row and the
-      // accumulator rescale (a multiply by 1) is skipped for the whole wave.
-      // (Measured on MI355X: pays for single-tile waves and for the LDS-shared
-      // workgroups of long row tiles; costs more than it saves for the
-      // multi-tile single waves of verify and the shared-prefix pass.)
-      rescale[nt] = (NT > 1 && W == 1) || __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0;
+      // While no reference maximum moves, alpha is exactly 1 on every row and
+      // the accumulator rescale (a multiply by 1) is skipped for the whole wave.
+      rescale[nt] = __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0;
       // rescale factors move to the accumulator layout: lane holds rows 4*grp + jj
       if (rescale[nt]) {
 #pragma unroll
