@@ -696,8 +696,10 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
     // One pair in flight per wave is enough to saturate HBM with two waves
     // per SIMD, and fewer bytes queued in the memory system shorten every
     // dependent access (measured on MI355X: 3-6 % faster than keeping two
-    // pairs in flight).  Multi-tile (verify) waves do more math per pair and
-    // keep the second pair in flight.
+    // pairs in flight).  Multi-tile verify waves, few and short, keep the
+    // second pair in flight at one wave per SIMD.  The shared-prefix pass has
+    // thousands of such waves: one pair each fits two waves per SIMD, which
+    // is 13 % faster there.
     if constexpr (W > 1) {
       // pair image in LDS: [K block 0][K block 1][V block 0][V block 1], each
       // page as laid out in the pool, so fragments are read at pool offsets
@@ -788,7 +790,7 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
           run(r, base_pos + 2 * pj * kBlk);
         }
       }
-    } else if constexpr (NT >= 2 && D * NT < 512) {
+    } else if constexpr (NT >= 2 && D * NT < 512 && !PREFIX) {
       Frag fa, fb;
       load(fa, 0);
       for (int pj = 0; pj < npairs; pj += 2) {
@@ -1266,9 +1268,10 @@ void attn_append_kernel(AttnParams p, InlineMeta im) {
 
 // Shared-prefix pass: one workgroup of W waves per (prefix unit, kv head);
 // wave w takes 16 * NT query rows of one group of sequences over one
-// partition of their common prefix.  (Measured on MI355X: 2 tiles per wave
-// with the next pair in flight is best; several waves per workgroup reading
-// the same pages, or 4 tiles per wave, are not faster.)
+// partition of their common prefix.  (Measured on MI355X: 2 tiles per wave,
+// one pair in flight and two waves per SIMD is best; the next pair in flight
+// at one wave per SIMD, several waves per workgroup reading the same pages or
+// sharing them through LDS, or 4 tiles per wave, are slower.)
 template <int D>
 struct PrefixShape {
   static constexpr int NT = D <= 128 ? 2 : 1;  // row tiles per wave
@@ -1276,7 +1279,8 @@ struct PrefixShape {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(64 * PrefixShape<D>::W) void prefix_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * PrefixShape<D>::W) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
+void prefix_kernel(AttnParams p) {
   constexpr int NT = PrefixShape<D>::NT;
   const int unit = blockIdx.x / p.hkv;
   const int kvh = blockIdx.x - unit * p.hkv;
