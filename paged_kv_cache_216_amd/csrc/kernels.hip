@@ -1274,12 +1274,13 @@ void attn_append_kernel(AttnParams p, InlineMeta im) {
 // sharing them through LDS, or 4 tiles per wave, are slower.)
 template <int D>
 struct PrefixShape {
-  static constexpr int NT = D <= 128 ? 2 : 1;  // row tiles per wave
-  static constexpr int W = 1;                  // waves per workgroup
+  static constexpr int NT = D <= 128 ? 2 : 1;            // row tiles per wave
+  static constexpr int W = 1;                            // waves per workgroup
+  static constexpr int kWavesPerSimd = D <= 128 ? 2 : 1;  // resident waves per SIMD
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(64 * PrefixShape<D>::W) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
+__global__ __launch_bounds__(64 * PrefixShape<D>::W) __attribute__((amdgpu_waves_per_eu(PrefixShape<D>::kWavesPerSimd)))
 void prefix_kernel(AttnParams p) {
   constexpr int NT = PrefixShape<D>::NT;
   const int unit = blockIdx.x / p.hkv;
@@ -1452,6 +1453,14 @@ int prefix_rows_per_unit(int head_dim) {
     case 64: return 16 * PrefixShape<64>::NT * PrefixShape<64>::W;
     case 128: return 16 * PrefixShape<128>::NT * PrefixShape<128>::W;
     default: return 16 * PrefixShape<256>::NT * PrefixShape<256>::W;
+  }
+}
+
+int prefix_waves_per_cu(int head_dim) {
+  switch (head_dim) {
+    case 64: return 4 * PrefixShape<64>::kWavesPerSimd;
+    case 128: return 4 * PrefixShape<128>::kWavesPerSimd;
+    default: return 4 * PrefixShape<256>::kWavesPerSimd;
   }
 }
 

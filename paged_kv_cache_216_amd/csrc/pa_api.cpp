@@ -65,6 +65,13 @@ struct ProfEvent {
   hipEvent_t start, stop;
 };
 
+// A group of copy-on-write forks found by the shared-prefix detection:
+// tokens all of them hold in the same blocks (and every query row sees), and
+// how many sequences of the call it has.
+struct PrefixGroup {
+  int shared, members;
+};
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
@@ -77,6 +84,7 @@ struct pa_pool {
   int32_t* block_table = nullptr;
   int32_t* seq_len = nullptr;
   bool host_only = false;
+  int num_cus = 256;  // compute units of the pool's device
   // metadata ring
   Stage stage[kStages];
   int next_stage = 0;
@@ -104,6 +112,7 @@ struct pa_pool {
   // shared-prefix pass: partitions of each sequence done by the pass (0 = none)
   std::vector<int> pre_parts;
   std::vector<std::pair<int32_t, int>> pre_scratch;
+  std::vector<PrefixGroup> pre_groups;
   std::vector<pa::PrefixUnit> pre_units;
   std::vector<pa::PrefixMember> pre_members;
   int plan_pre_units = 0;
@@ -334,6 +343,7 @@ constexpr int kPrefixMinGroup = 4;
 
 void find_prefix_groups(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, int k_draft) {
   p->pre_parts.assign(n_seq, 0);
+  p->pre_groups.clear();
   auto& pairs = p->pre_scratch;
   pairs.clear();
   if (pt <= 0 || (p->dtype != PA_F16 && p->dtype != PA_BF16) || n_seq < kPrefixMinGroup) return;
@@ -358,8 +368,10 @@ void find_prefix_groups(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, i
         while (j < blocks && tk[j] == t0[j]) ++j;
         blocks = j;
       }
-      const int q_parts = std::min(blocks * pa::kBlock, limit) / pt;
+      const int shared = std::min(blocks * pa::kBlock, limit);
+      const int q_parts = shared / pt;
       if (q_parts > 0) {
+        p->pre_groups.push_back({shared, static_cast<int>(b - a)});
         for (size_t k = a; k < b; ++k) {
           p->pre_parts[pairs[k].second] = q_parts;
           pairs[out++] = pairs[k];
@@ -369,6 +381,41 @@ void find_prefix_groups(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, i
     a = b;
   }
   pairs.resize(out);
+}
+
+// Partition length for a call with shared-prefix groups, when the library
+// chooses it.  The pass runs one wave per (prefix partition, row block, kv
+// head); when those waves exceed what the device holds at once, the last,
+// partial generation costs as long as a full one.  Longer partitions (up to
+// twice pt0) are then tried, and the one with the shortest critical path
+// (generations x tokens per wave) is taken, the shortest on ties.  (Measured
+// on MI355X, 64 forks of a 4,096-token prefix with 5 drafts: 512-token
+// partitions give 2,560 waves for 2,048 slots and a 105 us step; 608 gives
+// 1,920 waves and 88 us.)
+int prefix_partition(const pa_pool* p, int pt0, int rows) {
+  if (p->pre_groups.empty()) return pt0;
+  const int64_t rpw = pa::prefix_rows_per_unit(p->head_dim);
+  const int64_t resident = static_cast<int64_t>(p->num_cus) * pa::prefix_waves_per_cu(p->head_dim);
+  auto waves = [&](int pt) {
+    int64_t w = 0;
+    for (const PrefixGroup& g : p->pre_groups)
+      w += static_cast<int64_t>(g.shared / pt) * ((static_cast<int64_t>(g.members) * rows + rpw - 1) / rpw) * p->hkv;
+    return w;
+  };
+  const int64_t w0 = waves(pt0);
+  if (w0 <= resident) return pt0;
+  int best = pt0;
+  int64_t best_cost = (w0 + resident - 1) / resident * pt0;
+  for (int pt = pt0 + 32; pt <= 2 * pt0; pt += 32) {
+    const int64_t w = waves(pt);
+    if (w == 0) break;  // no whole partition left in any prefix
+    const int64_t cost = (w + resident - 1) / resident * pt;
+    if (cost < best_cost) {
+      best = pt;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 // Counters for the in-launch merge: at least n, zeroed when (re)allocated.
@@ -525,6 +572,15 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
 
   // forks sharing a prefix: its partitions are computed once for all of them
   find_prefix_groups(p, seq_ids, n_seq, pt, k_draft);
+  if (partition_tokens == 0 && pt > 0) {
+    // a longer partition never needs more workspace than the one checked above
+    const int best = prefix_partition(p, pt, rows);
+    if (best != pt) {
+      pt = best;
+      slots = count_parts(p, n_seq, pt);
+      find_prefix_groups(p, seq_ids, n_seq, pt, k_draft);
+    }
+  }
 
   // reuse the device plan when the batch, its partition structure and the
   // shared-prefix grouping are unchanged
@@ -700,6 +756,10 @@ int pa_create_pool(pa_pool** out, int num_blocks, int block_size, int num_kv_hea
   p->seq_len = seq_len_dev;
   p->host_only = (ndev == 0);
   if (!p->host_only) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      p->num_cus = cus;
     for (Stage& st : p->stage) {
       hipError_t e = hipEventCreateWithFlags(&st.done, hipEventDisableTiming);
       if (e != hipSuccess) {

@@ -313,7 +313,7 @@ def test_full_long():
 
 
 def test_full_verify():
-    _full(make_verify(), [0, 33, 63])
+    _full(make_verify(), [0, 17, 33, 50, 63])
 
 
 def test_many_partitions_fused_merge_and_repeat():
