@@ -702,14 +702,22 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
     // is 13 % faster there.
     if constexpr (W > 1) {
       // pair image in LDS: [K block 0][K block 1][V block 0][V block 1], each
-      // page as laid out in the pool, so fragments are read at pool offsets
+      // page as laid out in the pool, so fragments are read at pool offsets.
+      // A ring of kRing images: pairs pj + 1 .. pj + kRing - 1 load straight
+      // from the pool into LDS (buffer loads with an LDS destination, no
+      // staging registers) while the waves compute on pair pj.
       constexpr int kPair = 4 * kPageBytes;
       constexpr int kPer = kPair / (16 * 64 * W);  // 16-byte chunks per thread
+      constexpr int kChunksPerPage = kPageBytes / 16;
+      constexpr int kRing = 3;
       static_assert(kPer * 16 * 64 * W == kPair, "pair image must split evenly");
-      __shared__ __attribute__((aligned(16))) char lds[2][kPair];
-      const int tid = threadIdx.x;
-      u32x4 st[kPer];
-      auto gload = [&](int pj) {
+      static_assert(kChunksPerPage % 64 == 0, "a wave's 64 chunks lie in one page");
+      static_assert(kRing >= 2 && kRing <= 4 && (kRing - 2) * kPer <= 63, "the waits below cover up to two later pairs");
+      __shared__ __attribute__((aligned(16))) char lds[kRing][kPair];
+      const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+      // each load instruction fills 64 consecutive 16-byte chunks of one page:
+      // lane l writes chunk c0 + l (the LDS address is the wave's base plus 16 l)
+      auto dma = [&](int pj, int b) {
         const int j = 2 * pj;
         const int bytes0 = j < cnt ? kPageBytes : 0;
         const int bytes1 = j + 1 < cnt ? kPageBytes : 0;
@@ -719,15 +727,12 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
                                               page_rsrc(vpool + off0, bytes0), page_rsrc(vpool + off1, bytes1)};
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
-          const int ci = tid + 64 * W * k;  // chunk of the pair image
-          const int pg = ci / (kPageBytes / 16);
-          st[k] = page_load16<NTL>(rs[pg], (ci - pg * (kPageBytes / 16)) * 16);
+          const int c0 = wave * 64 + 64 * W * k;  // first chunk of the wave's 64
+          const int pg = c0 / kChunksPerPage;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs[pg], (__attribute__((address_space(3))) void*)(&lds[b][c0 * 16]), 16,
+              (c0 - pg * kChunksPerPage + lane) * 16, 0, 0, NTL ? 2 : 0);
         }
-      };
-      auto lstore = [&](int b) {
-#pragma unroll
-        for (int k = 0; k < kPer; ++k)
-          *reinterpret_cast<u32x4*>(&lds[b][(tid + 64 * W * k) * 16]) = st[k];
       };
       auto lfrag = [&](Frag& f, int b) {
         const char* kb = lds[b];
@@ -745,19 +750,39 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
           f.v1[c] = *reinterpret_cast<const u32x2*>(vb + kPageBytes + o);
         }
       };
-      if (npairs > 0) {
-        gload(0);
-        lstore(0);
-        __syncthreads();
-      }
+      // s_waitcnt immediates (gfx9 layout: vector-memory count in bits 3:0
+      // and 15:14): count <= n, the other counters not waited on
+      constexpr int kNoOther = (7 << 4) | (15 << 8);
+      constexpr int kWait1 = kNoOther | (kPer & 15) | ((kPer >> 4) << 14);
+      constexpr int kWait2 = kNoOther | ((2 * kPer) & 15) | ((2 * kPer) >> 4 << 14);
+      // Loads into registers (queries, table entries) complete here, before
+      // the ring starts: otherwise the compiler's waits for them sit inside
+      // the loop, where their counts would also cover the pairs in flight.
+      __builtin_amdgcn_s_waitcnt(kNoOther);
+#pragma unroll
+      for (int r = 0; r < kRing - 1; ++r)
+        if (r < npairs) dma(r, r);
       for (int pj = 0; pj < npairs; ++pj) {
-        if (pj + 1 < npairs) gload(pj + 1);
+        // This wave's share of pair pj has landed (only the loads of the
+        // pairs after it may still run); after the barrier every wave's share
+        // has, and every wave has read the image of pair pj - 1 (its
+        // fragments fed the MFMAs before the wave got here), which the load
+        // of pair pj + kRing - 1 then overwrites.  A bare s_barrier: a fence
+        // would make the compiler wait for the later pairs' loads as well.
+        const int later = min(npairs - 1 - pj, kRing - 2);  // pairs issued after pj
+        if (later >= 2)
+          __builtin_amdgcn_s_waitcnt(kWait2);
+        else if (later == 1)
+          __builtin_amdgcn_s_waitcnt(kWait1);
+        else
+          __builtin_amdgcn_s_waitcnt(kNoOther);
+        __builtin_amdgcn_s_barrier();
+        if (pj + kRing - 1 < npairs) dma(pj + kRing - 1, (pj + kRing - 1) % kRing);
         Frag f;
-        lfrag(f, pj & 1);
+        lfrag(f, pj % kRing);
         process(f, base_pos + 2 * pj * kBlk, pool_end);
-        if (pj + 1 < npairs) lstore((pj + 1) & 1);
-        __syncthreads();
       }
+      __syncthreads();  // the next table chunk refills the ring
     } else if constexpr (Q8) {
       auto run = [&](Frag8& r, int pos0) {
         Frag f;
