@@ -450,7 +450,7 @@ __device__ inline uint32_t page_load4(__amdgpu_buffer_rsrc_t r, int byte_off) {
 template <typename T, int D, int NT, bool NTL, bool FUSED, bool PREFIX = false, bool Q8 = false, int W = 1>
 __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) {
   static_assert(!(Q8 && PREFIX), "E4M3 pools take no shared-prefix pass");
-  static_assert(W == 1 || !(Q8 || FUSED || PREFIX), "LDS-shared pairs: plain 16-bit path only");
+  static_assert(W == 1 || !(Q8 || FUSED), "LDS-shared pairs: 16-bit pools, no fused append");
   using Op = typename MfmaOp<T>::type;
   constexpr int KS = D / 32;  // QK k-steps per block
   constexpr int DC = D / 16;  // output dim chunks
@@ -1295,8 +1295,9 @@ void attn_append_kernel(AttnParams p, InlineMeta im) {
 // wave w takes 16 * NT query rows of one group of sequences over one
 // partition of their common prefix.  (Measured on MI355X: 2 tiles per wave,
 // one pair in flight and two waves per SIMD is best; the next pair in flight
-// at one wave per SIMD, several waves per workgroup reading the same pages or
-// sharing them through LDS, or 4 tiles per wave, are slower.)
+// at one wave per SIMD, several waves per workgroup reading the same pages,
+// four waves sharing each pair through the LDS ring of the row tiles (48 us
+// against 42 us for the 64-fork verify), or 4 tiles per wave, are slower.)
 template <int D>
 struct PrefixShape {
   static constexpr int NT = D <= 128 ? 2 : 1;            // row tiles per wave
@@ -1311,8 +1312,12 @@ void prefix_kernel(AttnParams p) {
   const int unit = blockIdx.x / p.hkv;
   const int kvh = blockIdx.x - unit * p.hkv;
   const PrefixUnit pu = p.pre_units[unit];
+  // With several waves per workgroup, a wave past the group's rows still
+  // loads its share of every pair and meets every barrier; its queries repeat
+  // the group's last row and nothing of it is stored.  A lone wave past them
+  // has nothing to do.
   const int row0 = pu.row0 + static_cast<int>(threadIdx.x >> 6) * 16 * NT;
-  if (row0 >= pu.group_rows) return;  // whole wave past the group's rows
+  if (PrefixShape<D>::W == 1 && row0 >= pu.group_rows) return;
   Unit u{};
   u.seq = pu.seq;
   u.n_raw = pu.prefix_tokens;
@@ -1327,7 +1332,7 @@ void prefix_kernel(AttnParams p) {
   u.trows = 1 << 24;  // no causal limit: the prefix precedes every query row
   u.clip_row = 1 << 24;
   // the prefix blocks are read by every row block of the group: cached loads
-  attn_body16<T, D, NT, false, false, true>(p, u, kvh);
+  attn_body16<T, D, NT, false, false, true, false, PrefixShape<D>::W>(p, u, kvh);
 }
 
 // Exact merge of one output row of a split sequence, one 256-thread workgroup
@@ -1481,11 +1486,11 @@ int prefix_rows_per_unit(int head_dim) {
   }
 }
 
-int prefix_waves_per_cu(int head_dim) {
+int prefix_units_per_cu(int head_dim) {
   switch (head_dim) {
-    case 64: return 4 * PrefixShape<64>::kWavesPerSimd;
-    case 128: return 4 * PrefixShape<128>::kWavesPerSimd;
-    default: return 4 * PrefixShape<256>::kWavesPerSimd;
+    case 64: return 4 * PrefixShape<64>::kWavesPerSimd / PrefixShape<64>::W;
+    case 128: return 4 * PrefixShape<128>::kWavesPerSimd / PrefixShape<128>::W;
+    default: return 4 * PrefixShape<256>::kWavesPerSimd / PrefixShape<256>::W;
   }
 }
 

@@ -144,8 +144,8 @@ hipError_t launch_merge(DType dt, const AttnParams& p, hipStream_t stream);
 hipError_t launch_prefix(DType dt, const AttnParams& p, hipStream_t stream);
 // Query rows one workgroup of the shared-prefix pass takes, for a head dim.
 int prefix_rows_per_unit(int head_dim);
-// waves of the shared-prefix pass one compute unit holds at once
-int prefix_waves_per_cu(int head_dim);
+// workgroups of the shared-prefix pass one compute unit holds at once
+int prefix_units_per_cu(int head_dim);
 // Workgroups of 64 threads that the append work of `p` needs.
 int append_blocks64(const AppendParams& p);
 // Query rows one single-wave attention unit takes at most, for a head dim.

@@ -384,8 +384,8 @@ void find_prefix_groups(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, i
 }
 
 // Partition length for a call with shared-prefix groups, when the library
-// chooses it.  The pass runs one wave per (prefix partition, row block, kv
-// head); when those waves exceed what the device holds at once, the last,
+// chooses it.  The pass runs one workgroup per (prefix partition, row block,
+// kv head); when those exceed what the device holds at once, the last,
 // partial generation costs as long as a full one.  Longer partitions (up to
 // twice pt0) are then tried, and the one with the shortest critical path
 // (generations x tokens per wave) is taken, the shortest on ties.  (Measured
@@ -395,8 +395,8 @@ void find_prefix_groups(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, i
 int prefix_partition(const pa_pool* p, int pt0, int rows) {
   if (p->pre_groups.empty()) return pt0;
   const int64_t rpw = pa::prefix_rows_per_unit(p->head_dim);
-  const int64_t resident = static_cast<int64_t>(p->num_cus) * pa::prefix_waves_per_cu(p->head_dim);
-  auto waves = [&](int pt) {
+  const int64_t resident = static_cast<int64_t>(p->num_cus) * pa::prefix_units_per_cu(p->head_dim);
+  auto waves = [&](int pt) {  // workgroups of the pass
     int64_t w = 0;
     for (const PrefixGroup& g : p->pre_groups)
       w += static_cast<int64_t>(g.shared / pt) * ((static_cast<int64_t>(g.members) * rows + rpw - 1) / rpw) * p->hkv;
