@@ -199,7 +199,11 @@ int pa_append_kv(pa_pool* pool, const int32_t* seq_ids, int n_seq, const int32_t
  *   lse          device float [n_seq][num_q_heads] (natural-log log-sum-exp of
  *                the scaled scores) or NULL
  *   partition_tokens  0 = library choice (512 tokens, or 8 per query row
- *                of a kv head when that is more); otherwise a positive
+ *                of a kv head when that is more; for calls with shared
+ *                prefixes (below) a longer one, up to twice that, when it
+ *                lets the shared-prefix launch run in fewer rounds of
+ *                resident workgroups -- never more workspace than the
+ *                default needs); otherwise a positive
  *                multiple of 32: contexts longer than this are cut into
  *                partitions processed in parallel and merged exactly by their
  *                log-sum-exp; a value >= the longest context disables the split
