@@ -323,6 +323,33 @@ def measured_traffic(workload: str, kernel: str):
     return None
 
 
+def copy_reference():
+    """A plain 1 GiB device-to-device copy on the same GPU, timed with events
+    after the timed region: what a simple streaming kernel reaches on this machine
+    (bytes read + written / time), as context for the fraction of the 8 TB/s
+    specification the attention reaches."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    reps = 10
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    gbs = 2 * n / (ms * 1e-3) / 1e9
+    return {"copy_gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_GBS, 4),
+            "what": "1 GiB device-to-device copy (torch copy_), read + written bytes / time, 10 repetitions"}
+
+
 PCIE_GBS = 64.0  # PCIe 5.0 x16, one direction, the MI355X host link
 
 
@@ -458,6 +485,7 @@ def main():
         st = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
         pct = {"p50": round(float(np.percentile(st, 50)), 2), "p90": round(float(np.percentile(st, 90)), 2),
                "p99": round(float(np.percentile(st, 99)), 2), "mean": round(float(st.mean()), 2)}
+    hbm_ref = None if args.no_profile_events else copy_reference()
     dec_b = decode_bytes(w, EB[cd])
     app_b = append_bytes(w, EB[cd])
     step_b = dec_b + app_b
@@ -523,6 +551,7 @@ def main():
                        "pa_append_attend (append and attention launches)" if reps[0].t_new and not args.separate else
                        "pa_append_kv + attention" if reps[0].t_new else "attention"),
         "roofline": roof,
+        "hbm_reference": hbm_ref,
     }
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
