@@ -61,6 +61,30 @@ def test_prefill_chunk_matches_oracle(dtype, head_dim, g, chunk, pt):
     assert_close(out, lse, ro, rl, dtype, f"prefill C={chunk}")
 
 
+@pytest.mark.parametrize("dtype,head_dim,g,chunk,cached,pt", [
+    ("bf16", 128, 4, 70, 1500, 0),     # 280 rows, tiles of 128, unsplit: 99 blocks, two table chunks
+    ("f16", 256, 2, 40, 1300, 4096),   # 80 rows, tiles of 64, forced unsplit: 84 blocks, 8 loads per thread
+    ("bf16", 64, 8, 30, 2100, 0),      # 240 rows; first partition 1,920 tokens (two chunks), merged
+])
+def test_prefill_long_context_crosses_table_chunks(dtype, head_dim, g, chunk, cached, pt):
+    """Row tiles over contexts longer than one 64-entry chunk of the table:
+    the LDS ring of pairs drains and refills at each chunk boundary.  Outputs
+    and lse against the oracle for every chunk token and query head."""
+    _say(f"prefill long {dtype} D={head_dim} G={g} C={chunk} cached={cached} pt={pt}")
+    hkv = 2
+    w = make_custom(lengths=[cached, cached // 3], mode="verify", num_q_heads=g * hkv, num_kv_heads=hkv,
+                    head_dim=head_dim, dtype=dtype, seed=90 + head_dim, k_draft=chunk)
+    pair = Pair(w)
+    pair.fill()
+    pair.append_step_rows()
+    pair.check_pools_and_tables()
+    seqs = list(range(w.batch))
+    out, lse = _prefill(pair, seqs, pt)
+    torch.cuda.synchronize()
+    ro, rl = oracle_decode(pair, seqs, w.q, w.scale, k_draft=chunk)
+    assert_close(out, lse, ro, rl, dtype, f"prefill long C={chunk}")
+
+
 def test_prefill_equals_verify_bitwise_and_repeats():
     """pa_prefill is pa_verify with k_draft = chunk: bitwise equal results,
     and a second identical call repeats them."""
