@@ -92,8 +92,11 @@ typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
  * block tables but enqueues no device work (pa_append_kv then takes NULL rows;
  * pa_decode / pa_verify return PA_ERR_STATE).
  * The library allocates, for the pool's lifetime, a ring of pinned host
- * buffers that the kernels read per-call metadata from, and a small device
- * buffer for the attention work plan; it never allocates pool memory. */
+ * buffers that the kernels read per-call metadata from, and three small
+ * device buffers: the attention work plan, the counters of the in-launch
+ * merge (zero between launches), and the E4M3 scales once set; it never
+ * allocates pool memory.  The plan and the counters grow (a device-wide
+ * synchronisation) when a call needs more than any call before. */
 int pa_create_pool(pa_pool** out, int num_blocks, int block_size, int num_kv_heads,
                    int head_dim, int dtype, void* k_pool, void* v_pool,
                    int32_t* block_table_dev, int32_t* seq_len_dev, int max_seqs,
