@@ -485,6 +485,7 @@ def main():
         st = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
         pct = {"p50": round(float(np.percentile(st, 50)), 2), "p90": round(float(np.percentile(st, 90)), 2),
                "p99": round(float(np.percentile(st, 99)), 2), "mean": round(float(st.mean()), 2)}
+    pt_used, prefix_wgs = reps[0].cache.last_partition()
     hbm_ref = None if args.no_profile_events else copy_reference()
     dec_b = decode_bytes(w, EB[cd])
     app_b = append_bytes(w, EB[cd])
@@ -538,6 +539,7 @@ def main():
                    "kv_cache": cd, "batch": w.batch, "seed": w.seed,
                    "replicas": args.replicas,
                    "partition_tokens": pt if pt > 0 else ("unsplit" if pt < 0 else "library choice"),
+                   "partition_tokens_used": pt_used, "shared_prefix_workgroups": prefix_wgs,
                    "bytes_per_step": step_b, "decode_bytes": dec_b, "append_bytes": app_b,
                    "cached_tokens": int(sum(step_lengths(w))), "attention_flops": flops},
         "kernel_us": {"attention": round(1e3 * kern[0][0] / max(1, kern[0][1]), 2),

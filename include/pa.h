@@ -314,6 +314,12 @@ int pa_get_refcount(const pa_pool* pool, int block_id, int* rc);
 int pa_num_free_blocks(const pa_pool* pool, int* n);
 /* The free list, front first (out may be NULL to query the count). */
 int pa_get_free_list(const pa_pool* pool, int32_t* out, int cap, int* n);
+/* The split-KV partition length (tokens) the pool's last successful
+ * pa_decode / pa_verify / pa_prefill / pa_append_attend call used -- the
+ * library's choice when it was given 0 -- and the number of shared-prefix
+ * workgroups that call launched; *partition_tokens = 0 when nothing was
+ * split (and before the first call). */
+int pa_last_partition(const pa_pool* pool, int* partition_tokens, int* prefix_units);
 
 const char* pa_strerror(int status);
 const char* pa_last_error(void);

@@ -53,6 +53,7 @@ SIGNATURES = {
     "pa_get_block_table": (c_int, [c_void_p, c_int, c_i32p, c_int, c_intp, c_intp]),
     "pa_get_refcount": (c_int, [c_void_p, c_int, c_intp]),
     "pa_num_free_blocks": (c_int, [c_void_p, c_intp]),
+    "pa_last_partition": (c_int, [c_void_p, c_intp, c_intp]),
     "pa_get_free_list": (c_int, [c_void_p, c_i32p, c_int, c_intp]),
     "pa_strerror": (ctypes.c_char_p, [c_int]),
     "pa_last_error": (ctypes.c_char_p, []),

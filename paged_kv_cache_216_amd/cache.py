@@ -212,6 +212,12 @@ class PagedKVCache:
         abi.check(self.lib.pa_num_free_blocks(self.handle, ctypes.byref(n)))
         return n.value
 
+    def last_partition(self):
+        """(partition tokens, shared-prefix workgroups) of the last attention call."""
+        pt, pu = ctypes.c_int(), ctypes.c_int()
+        abi.check(self.lib.pa_last_partition(self.handle, ctypes.byref(pt), ctypes.byref(pu)))
+        return pt.value, pu.value
+
     def free_list(self):
         n = ctypes.c_int()
         abi.check(self.lib.pa_get_free_list(self.handle, None, 0, ctypes.byref(n)))

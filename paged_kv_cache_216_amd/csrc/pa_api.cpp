@@ -85,6 +85,7 @@ struct pa_pool {
   int32_t* seq_len = nullptr;
   bool host_only = false;
   int num_cus = 256;  // compute units of the pool's device
+  int last_pt = 0, last_prefix_units = 0;  // of the last attention call
   // metadata ring
   Stage stage[kStages];
   int next_stage = 0;
@@ -700,6 +701,8 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
     if (e != hipSuccess) return hip_err(e, "merge kernel");
     prof_end(p, stream, &ev);
   }
+  p->last_pt = slots > 0 ? pt : 0;
+  p->last_prefix_units = ak.n_pre_units * p->hkv;
   return st ? release_stage(st, stream) : PA_OK;
 }
 
@@ -1097,6 +1100,13 @@ int pa_get_refcount(const pa_pool* p, int block_id, int* rc) {
 int pa_num_free_blocks(const pa_pool* p, int* n) {
   if (!p || !n) return set_err(PA_ERR_INVALID, "NULL argument");
   *n = p->bp.num_free();
+  return PA_OK;
+}
+
+int pa_last_partition(const pa_pool* p, int* partition_tokens, int* prefix_units) {
+  if (!p || !partition_tokens || !prefix_units) return set_err(PA_ERR_INVALID, "NULL argument");
+  *partition_tokens = p->last_pt;
+  *prefix_units = p->last_prefix_units;
   return PA_OK;
 }
 

@@ -297,6 +297,7 @@ def _full(w, samples):
     torch.cuda.synchronize()
     _say(f"full {w.name}: oracle on {samples}")
     _sampled(pair, w, out, lse, samples, w.k_draft)
+    return pair
 
 
 def test_full_gqa70b():
@@ -313,7 +314,18 @@ def test_full_long():
 
 
 def test_full_verify():
-    _full(make_verify(), [0, 17, 33, 50, 63])
+    pair = _full(make_verify(), [0, 17, 33, 50, 63])
+    # The library chose the partition: at the default 512 tokens the shared-
+    # prefix pass would need 8 partitions x 40 row blocks x 8 kv heads = 2,560
+    # workgroups, more than one round of the 8 per CU the device holds at
+    # once; the chosen length (a multiple of 32, at most twice the default)
+    # fits the pass into one round.
+    pt, prefix_wgs = pair.gpu.last_partition()
+    resident = 8 * torch.cuda.get_device_properties(0).multi_processor_count
+    assert pt % 32 == 0 and 512 <= pt <= 1024, pt
+    assert prefix_wgs == (4096 // pt) * 40 * 8, (pt, prefix_wgs)
+    if 8 * 40 * 8 > resident:
+        assert prefix_wgs <= resident, (pt, prefix_wgs, resident)
 
 
 def test_many_partitions_fused_merge_and_repeat():
