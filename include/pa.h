@@ -72,8 +72,7 @@ typedef enum {
  * to float32, clamped to [-448, 448] and rounded to the nearest code, ties to
  * the even code; the attention uses decode(code) * scale[h], in fp32.  An
  * 8-bit cache halves the bytes a decode step reads while the softmax stays at
- * full precision (ranksignal.fr post 218, "Quantifier").  The 8-bit pools do
- * not take the shared-prefix pass. */
+ * full precision (ranksignal.fr post 218, "Quantifier"). */
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
 
 /* Create a pool over caller-owned device memory.
@@ -222,7 +221,7 @@ int pa_append_kv(pa_pool* pool, const int32_t* seq_ids, int n_seq, const int32_t
  * shared by sequences of one prompt: "PagedAttention, décodage spéculatif,
  * MoE et Blackwell", section 1; kenji.blog page, section 4.2; reusing the KV
  * cache of a common prefix: ranksignal.fr post 218, "Mettre en cache").
- * Needs the split (a workspace) and a 16-bit dtype.  Results equal the
+ * Needs the split (a workspace) and a 16-bit or E4M3 pool.  Results equal the
  * per-sequence computation up to floating-point summation order.
  * Softmax and accumulation are fp32; out is rounded to dtype (nearest even).
  * Graph capture: engines replay a recorded launch sequence instead of

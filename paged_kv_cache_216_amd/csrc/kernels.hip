@@ -449,7 +449,6 @@ __device__ inline uint32_t page_load4(__amdgpu_buffer_rsrc_t r, int byte_off) {
 // workgroup's), so the barriers line up.
 template <typename T, int D, int NT, bool NTL, bool FUSED, bool PREFIX = false, bool Q8 = false, int W = 1>
 __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) {
-  static_assert(!(Q8 && PREFIX), "E4M3 pools take no shared-prefix pass");
   static_assert(W == 1 || !(Q8 || FUSED), "LDS-shared pairs: 16-bit pools, no fused append");
   using Op = typename MfmaOp<T>::type;
   constexpr int KS = D / 32;  // QK k-steps per block
@@ -960,7 +959,7 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
           const int slot = m.slot_base + kvh * m.nparts + u.part;
           float* ap = p.ws_acc + (static_cast<size_t>(slot) * rows + (r - j * rows)) * D;
 #pragma unroll
-          for (int c = 0; c < DC; ++c) ap[16 * c + col] = acc[nt][c][jj];
+          for (int c = 0; c < DC; ++c) ap[16 * c + col] = acc[nt][c][jj] * vsc;  // (E4M3: the head's V scale)
         }
       }
       const int r = u.pre_row0 + nt * 16 + col;
@@ -1305,7 +1304,7 @@ struct PrefixShape {
   static constexpr int kWavesPerSimd = D <= 128 ? 2 : 1;  // resident waves per SIMD
 };
 
-template <typename T, int D>
+template <typename T, int D, bool Q8 = false>
 __global__ __launch_bounds__(64 * PrefixShape<D>::W) __attribute__((amdgpu_waves_per_eu(PrefixShape<D>::kWavesPerSimd)))
 void prefix_kernel(AttnParams p) {
   constexpr int NT = PrefixShape<D>::NT;
@@ -1332,7 +1331,7 @@ void prefix_kernel(AttnParams p) {
   u.trows = 1 << 24;  // no causal limit: the prefix precedes every query row
   u.clip_row = 1 << 24;
   // the prefix blocks are read by every row block of the group: cached loads
-  attn_body16<T, D, NT, false, false, true, false, PrefixShape<D>::W>(p, u, kvh);
+  attn_body16<T, D, NT, false, false, true, Q8, PrefixShape<D>::W>(p, u, kvh);
 }
 
 // Exact merge of one output row of a split sequence, one 256-thread workgroup
@@ -1514,6 +1513,13 @@ hipError_t launch_prefix(DType dt, const AttnParams& p, hipStream_t stream) {
         case 64: return go(prefix_kernel<_Float16, 64>, PrefixShape<64>::W);
         case 128: return go(prefix_kernel<_Float16, 128>, PrefixShape<128>::W);
         case 256: return go(prefix_kernel<_Float16, 256>, PrefixShape<256>::W);
+      }
+      break;
+    case kFP8:  // E4M3 codes, bf16 queries and partials
+      switch (p.head_dim) {
+        case 64: return go(prefix_kernel<__bf16, 64, true>, PrefixShape<64>::W);
+        case 128: return go(prefix_kernel<__bf16, 128, true>, PrefixShape<128>::W);
+        case 256: return go(prefix_kernel<__bf16, 256, true>, PrefixShape<256>::W);
       }
       break;
     default: break;

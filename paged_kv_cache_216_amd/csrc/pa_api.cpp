@@ -347,7 +347,7 @@ void find_prefix_groups(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, i
   p->pre_groups.clear();
   auto& pairs = p->pre_scratch;
   pairs.clear();
-  if (pt <= 0 || (p->dtype != PA_F16 && p->dtype != PA_BF16) || n_seq < kPrefixMinGroup) return;
+  if (pt <= 0 || p->dtype == PA_F32 || n_seq < kPrefixMinGroup) return;
   for (int i = 0; i < n_seq; ++i) {
     const std::vector<int32_t>& tab = p->bp.table(seq_ids[i]);
     if (p->lens[i] - k_draft >= pt && !tab.empty() && p->bp.refcount(tab[0]) > 1) pairs.push_back({tab[0], i});

@@ -111,6 +111,30 @@ def test_fp8_verify_shared_prefix_copy_on_write(head_dim, g, kd):
     assert_close(out, lse, ro, rl, "fp8", "fp8 verify")
 
 
+@pytest.mark.parametrize("prefix_len,k_draft", [(1100, 5), (2100, 1)])
+def test_fp8_shared_prefix_pass(prefix_len, k_draft):
+    """Six forks of one prefix on 8-bit pools: the prefix's whole 512-token
+    partitions run once for all six in the shared-prefix launch (codes
+    decoded with the head's scales, the V scale applied to the partials);
+    outputs and lse match the oracle over the stored codes."""
+    _say(f"fp8 shared-prefix pass prefix={prefix_len} k={k_draft}")
+    w = make_custom(lengths=[16, 77, 200, 512, 31, 100], mode="verify", num_q_heads=16, num_kv_heads=4,
+                    head_dim=128, dtype="bf16", seed=38 + k_draft, k_draft=k_draft, prefix_len=prefix_len)
+    pair = _pair(w)
+    pair.fill()
+    pair.append_step_rows()
+    pair.check_pools_and_tables()
+    seqs = list(range(w.batch))
+    pair.gpu.profile_enable(True)
+    out, lse = _attend(pair, seqs, w.q, k_draft=k_draft, pt=512)
+    torch.cuda.synchronize()
+    _, n_prefix = pair.gpu.profile_read(3)
+    pair.gpu.profile_enable(False)
+    assert n_prefix == 1, "the shared-prefix launch did not run"
+    ro, rl = oracle_decode(pair, seqs, w.q, w.scale, k_draft=k_draft)
+    assert_close(out, lse, ro, rl, "fp8", "fp8 shared-prefix pass")
+
+
 def test_fp8_append_attend_matches_separate_calls():
     """pa_append_attend on an 8-bit pool (one launch: append and attention)
     equals the two calls made one after the other, bitwise, and the oracle."""
