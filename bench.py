@@ -512,7 +512,7 @@ def main():
                       "so region / steps bounds its duration from above")
         # a fused launch also reads the new rows and writes them into the pool
         launch_b = dec_b + (app_b if fused else 0)
-        multi_wave = not one_tile and cd in ("f16", "bf16")  # LDS-shared row tiles
+        multi_wave = not one_tile and cd in ("f16", "bf16", "fp8")  # LDS-shared row tiles
         kname = "attn_append_kernel" if fused else ("tile_kernel" if multi_wave else "attn_kernel")
         achieved = launch_b / (attn_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",

@@ -449,7 +449,7 @@ __device__ inline uint32_t page_load4(__amdgpu_buffer_rsrc_t r, int byte_off) {
 // workgroup's), so the barriers line up.
 template <typename T, int D, int NT, bool NTL, bool FUSED, bool PREFIX = false, bool Q8 = false, int W = 1>
 __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) {
-  static_assert(W == 1 || !(Q8 || FUSED), "LDS-shared pairs: 16-bit pools, no fused append");
+  static_assert(W == 1 || !FUSED, "LDS-shared pairs: no fused append");
   using Op = typename MfmaOp<T>::type;
   constexpr int KS = D / 32;  // QK k-steps per block
   constexpr int DC = D / 16;  // output dim chunks
@@ -736,17 +736,33 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       auto lfrag = [&](Frag& f, int b) {
         const char* kb = lds[b];
         const char* vb = lds[b] + 2 * kPageBytes;
+        if constexpr (Q8) {
+          // the 8-bit operands at the offsets of the pool loads, turned into bf16
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const int o = ((4 * s + grp) * kBlk + col) * 16;
-          f.k0[s] = __builtin_bit_cast(Op, *reinterpret_cast<const u32x4*>(kb + o));
-          f.k1[s] = __builtin_bit_cast(Op, *reinterpret_cast<const u32x4*>(kb + kPageBytes + o));
-        }
+          for (int s = 0; s < KS; ++s) {
+            const int o = ((2 * s + (grp >> 1)) * kBlk + col) * 16 + 8 * (grp & 1);
+            f.k0[s] = __builtin_bit_cast(Op, fp8x8_to_bf16(*reinterpret_cast<const u32x2*>(kb + o)));
+            f.k1[s] = __builtin_bit_cast(Op, fp8x8_to_bf16(*reinterpret_cast<const u32x2*>(kb + kPageBytes + o)));
+          }
 #pragma unroll
-        for (int c = 0; c < DC; ++c) {
-          const int o = ((16 * c + col) * kBlk + 4 * grp) * 2;
-          f.v0[c] = *reinterpret_cast<const u32x2*>(vb + o);
-          f.v1[c] = *reinterpret_cast<const u32x2*>(vb + kPageBytes + o);
+          for (int c = 0; c < DC; ++c) {
+            const int o = (16 * c + col) * kBlk + 4 * grp;
+            f.v0[c] = fp8x4_to_bf16(*reinterpret_cast<const uint32_t*>(vb + o));
+            f.v1[c] = fp8x4_to_bf16(*reinterpret_cast<const uint32_t*>(vb + kPageBytes + o));
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            const int o = ((4 * s + grp) * kBlk + col) * 16;
+            f.k0[s] = __builtin_bit_cast(Op, *reinterpret_cast<const u32x4*>(kb + o));
+            f.k1[s] = __builtin_bit_cast(Op, *reinterpret_cast<const u32x4*>(kb + kPageBytes + o));
+          }
+#pragma unroll
+          for (int c = 0; c < DC; ++c) {
+            const int o = ((16 * c + col) * kBlk + 4 * grp) * 2;
+            f.v0[c] = *reinterpret_cast<const u32x2*>(vb + o);
+            f.v1[c] = *reinterpret_cast<const u32x2*>(vb + kPageBytes + o);
+          }
         }
       };
       // s_waitcnt immediates (gfx9 layout: vector-memory count in bits 3:0
@@ -1245,7 +1261,7 @@ struct TileShape {
   static constexpr int kRows = 16 * NT * W;    // query rows per workgroup
 };
 
-template <typename T, int D, bool NTL>
+template <typename T, int D, bool NTL, bool Q8 = false>
 __global__ __launch_bounds__(64 * TileShape<D>::W) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
 void tile_kernel(AttnParams p) {
   constexpr int NT = TileShape<D>::NT, W = TileShape<D>::W;
@@ -1271,7 +1287,7 @@ void tile_kernel(AttnParams p) {
   // nothing of it is stored
   u.trows = min(16 * NT, g_rows - wave * 16 * NT);
   u.clip_row = w.row0 + g_rows - 1;
-  attn_body16<T, D, NT, NTL, false, false, false, W>(p, u, kvh);
+  attn_body16<T, D, NT, NTL, false, false, Q8, W>(p, u, kvh);
 }
 
 // Attention and append in one launch: workgroups past the attention grid do
@@ -1429,11 +1445,11 @@ template <typename T, int D, bool NTL, bool Q8>
 hipError_t launch_attn_d(const AttnParams& p, const InlineMeta& m, hipStream_t stream) {
   // no fused fp32 path
   if (std::is_same_v<T, float> && p.t_new > 0) return hipErrorInvalidValue;
-  if constexpr (!std::is_same_v<T, float> && !Q8) {
+  if constexpr (!std::is_same_v<T, float>) {
     if (p.tile_rows > max_rows_for_head_dim(D)) {
       if (p.tile_rows != TileShape<D>::kRows || p.t_new > 0) return hipErrorInvalidValue;
       const dim3 grid(static_cast<unsigned>(p.n_units) * p.hkv);
-      hipLaunchKernelGGL((tile_kernel<T, D, NTL>), grid, dim3(64 * TileShape<D>::W), 0, stream, p);
+      hipLaunchKernelGGL((tile_kernel<T, D, NTL, Q8>), grid, dim3(64 * TileShape<D>::W), 0, stream, p);
       return hipGetLastError();
     }
   }
@@ -1469,7 +1485,7 @@ int max_rows_for_head_dim(int head_dim) { return head_dim <= 128 ? 64 : 32; }
 int tile_rows_for_call(int dtype, int head_dim, int rows) {
   const int one_wave = max_rows_for_head_dim(head_dim);
   if (rows <= one_wave) return rows;
-  if (dtype != kF16 && dtype != kBF16) return one_wave;  // fp32 and E4M3: single-wave tiles
+  if (dtype == kF32) return one_wave;  // fp32: single-wave tiles
   switch (head_dim) {
     case 64: return TileShape<64>::kRows;
     case 128: return TileShape<128>::kRows;

@@ -152,6 +152,25 @@ def test_prefill_fp8_pool():
     assert_close(out, lse, ro, rl, "fp8", "fp8 prefill")
 
 
+@pytest.mark.parametrize("head_dim,g,chunk,cached", [(64, 8, 20, 1400), (256, 2, 48, 1200)])
+def test_prefill_fp8_long_context_row_tiles(head_dim, g, chunk, cached):
+    """Row tiles of an E4M3 pool (pairs shared through the LDS ring as 8-bit
+    codes, decoded per wave) over a context longer than one 64-entry table
+    chunk, unsplit."""
+    w = make_custom(lengths=[cached, 60], mode="verify", num_q_heads=g * 2, num_kv_heads=2, head_dim=head_dim,
+                    dtype="bf16", seed=80 + head_dim, k_draft=chunk)
+    ks = np.array([0.03, 2.5], np.float32)
+    vs = np.array([4.0, 0.01], np.float32)
+    pair = Pair(w, cache_dtype="fp8", kv_scales=(ks, vs))
+    pair.fill()
+    pair.append_step_rows()
+    pair.check_pools_and_tables()
+    out, lse = _prefill(pair, [0, 1], 4096)
+    torch.cuda.synchronize()
+    ro, rl = oracle_decode(pair, [0, 1], w.q, w.scale, k_draft=chunk)
+    assert_close(out, lse, ro, rl, "fp8", "fp8 prefill, long context")
+
+
 def test_prefill_shared_prefix_forks():
     """Six forks of a 1,100-token prompt prefix each take a 24-token chunk:
     the prefix's whole partitions go through the shared-prefix pass (rows of
