@@ -1308,22 +1308,25 @@ void attn_append_kernel(AttnParams p, InlineMeta im) {
 
 // Shared-prefix pass: one workgroup of W waves per (prefix unit, kv head);
 // wave w takes 16 * NT query rows of one group of sequences over one
-// partition of their common prefix.  (Measured on MI355X: 2 tiles per wave,
-// one pair in flight and two waves per SIMD is best; the next pair in flight
-// at one wave per SIMD, several waves per workgroup reading the same pages,
-// four waves sharing each pair through the LDS ring of the row tiles (48 us
-// against 42 us for the 64-fork verify), or 4 tiles per wave, are slower.)
-template <int D>
+// partition of their common prefix.  (Measured on MI355X, 64-fork verify:
+// for 16-bit pools one wave per workgroup, 2 tiles, one pair in flight and two
+// waves per SIMD is best -- the next pair in flight at one wave per SIMD,
+// several waves reading the same pages, four waves sharing each pair through
+// the LDS ring of the row tiles (48 us against 42 us), or 4 tiles per wave
+// are slower; for E4M3 pools the four-wave LDS ring is best, 43 us against
+// 56 us: the 8-bit pair image is half the size.)
+template <int D, bool Q8 = false>
 struct PrefixShape {
   static constexpr int NT = D <= 128 ? 2 : 1;            // row tiles per wave
-  static constexpr int W = 1;                            // waves per workgroup
+  static constexpr int W = Q8 ? 4 : 1;                   // waves per workgroup
   static constexpr int kWavesPerSimd = D <= 128 ? 2 : 1;  // resident waves per SIMD
 };
 
 template <typename T, int D, bool Q8 = false>
-__global__ __launch_bounds__(64 * PrefixShape<D>::W) __attribute__((amdgpu_waves_per_eu(PrefixShape<D>::kWavesPerSimd)))
+__global__ __launch_bounds__((64 * PrefixShape<D, Q8>::W)) __attribute__((amdgpu_waves_per_eu((PrefixShape<D, Q8>::kWavesPerSimd))))
 void prefix_kernel(AttnParams p) {
-  constexpr int NT = PrefixShape<D>::NT;
+  using Shape = PrefixShape<D, Q8>;
+  constexpr int NT = Shape::NT;
   const int unit = blockIdx.x / p.hkv;
   const int kvh = blockIdx.x - unit * p.hkv;
   const PrefixUnit pu = p.pre_units[unit];
@@ -1332,7 +1335,7 @@ void prefix_kernel(AttnParams p) {
   // the group's last row and nothing of it is stored.  A lone wave past them
   // has nothing to do.
   const int row0 = pu.row0 + static_cast<int>(threadIdx.x >> 6) * 16 * NT;
-  if (PrefixShape<D>::W == 1 && row0 >= pu.group_rows) return;
+  if (Shape::W == 1 && row0 >= pu.group_rows) return;
   Unit u{};
   u.seq = pu.seq;
   u.n_raw = pu.prefix_tokens;
@@ -1347,7 +1350,7 @@ void prefix_kernel(AttnParams p) {
   u.trows = 1 << 24;  // no causal limit: the prefix precedes every query row
   u.clip_row = 1 << 24;
   // the prefix blocks are read by every row block of the group: cached loads
-  attn_body16<T, D, NT, false, false, true, Q8, PrefixShape<D>::W>(p, u, kvh);
+  attn_body16<T, D, NT, false, false, true, Q8, Shape::W>(p, u, kvh);
 }
 
 // Exact merge of one output row of a split sequence, one 256-thread workgroup
@@ -1493,20 +1496,32 @@ int tile_rows_for_call(int dtype, int head_dim, int rows) {
   }
 }
 
-int prefix_rows_per_unit(int head_dim) {
+namespace {
+template <bool Q8>
+int prefix_rows_t(int head_dim) {
   switch (head_dim) {
-    case 64: return 16 * PrefixShape<64>::NT * PrefixShape<64>::W;
-    case 128: return 16 * PrefixShape<128>::NT * PrefixShape<128>::W;
-    default: return 16 * PrefixShape<256>::NT * PrefixShape<256>::W;
+    case 64: return 16 * PrefixShape<64, Q8>::NT * PrefixShape<64, Q8>::W;
+    case 128: return 16 * PrefixShape<128, Q8>::NT * PrefixShape<128, Q8>::W;
+    default: return 16 * PrefixShape<256, Q8>::NT * PrefixShape<256, Q8>::W;
   }
 }
 
-int prefix_units_per_cu(int head_dim) {
+template <bool Q8>
+int prefix_units_t(int head_dim) {
   switch (head_dim) {
-    case 64: return 4 * PrefixShape<64>::kWavesPerSimd / PrefixShape<64>::W;
-    case 128: return 4 * PrefixShape<128>::kWavesPerSimd / PrefixShape<128>::W;
-    default: return 4 * PrefixShape<256>::kWavesPerSimd / PrefixShape<256>::W;
+    case 64: return 4 * PrefixShape<64, Q8>::kWavesPerSimd / PrefixShape<64, Q8>::W;
+    case 128: return 4 * PrefixShape<128, Q8>::kWavesPerSimd / PrefixShape<128, Q8>::W;
+    default: return 4 * PrefixShape<256, Q8>::kWavesPerSimd / PrefixShape<256, Q8>::W;
   }
+}
+}  // namespace
+
+int prefix_rows_per_unit(int dtype, int head_dim) {
+  return dtype == kFP8 ? prefix_rows_t<true>(head_dim) : prefix_rows_t<false>(head_dim);
+}
+
+int prefix_units_per_cu(int dtype, int head_dim) {
+  return dtype == kFP8 ? prefix_units_t<true>(head_dim) : prefix_units_t<false>(head_dim);
 }
 
 hipError_t launch_prefix(DType dt, const AttnParams& p, hipStream_t stream) {
@@ -1533,9 +1548,9 @@ hipError_t launch_prefix(DType dt, const AttnParams& p, hipStream_t stream) {
       break;
     case kFP8:  // E4M3 codes, bf16 queries and partials
       switch (p.head_dim) {
-        case 64: return go(prefix_kernel<__bf16, 64, true>, PrefixShape<64>::W);
-        case 128: return go(prefix_kernel<__bf16, 128, true>, PrefixShape<128>::W);
-        case 256: return go(prefix_kernel<__bf16, 256, true>, PrefixShape<256>::W);
+        case 64: return go(prefix_kernel<__bf16, 64, true>, PrefixShape<64, true>::W);
+        case 128: return go(prefix_kernel<__bf16, 128, true>, PrefixShape<128, true>::W);
+        case 256: return go(prefix_kernel<__bf16, 256, true>, PrefixShape<256, true>::W);
       }
       break;
     default: break;

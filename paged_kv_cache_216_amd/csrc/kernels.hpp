@@ -143,9 +143,9 @@ hipError_t launch_merge(DType dt, const AttnParams& p, hipStream_t stream);
 // The shared-prefix pass (16-bit dtypes); run before launch_attention.
 hipError_t launch_prefix(DType dt, const AttnParams& p, hipStream_t stream);
 // Query rows one workgroup of the shared-prefix pass takes, for a head dim.
-int prefix_rows_per_unit(int head_dim);
+int prefix_rows_per_unit(int dtype, int head_dim);
 // workgroups of the shared-prefix pass one compute unit holds at once
-int prefix_units_per_cu(int head_dim);
+int prefix_units_per_cu(int dtype, int head_dim);
 // Workgroups of 64 threads that the append work of `p` needs.
 int append_blocks64(const AppendParams& p);
 // Query rows one single-wave attention unit takes at most, for a head dim.

@@ -141,7 +141,7 @@ int acquire_stage(pa_pool* p, size_t words, Stage** out) {
   }
   if (words > st.cap) {
     const size_t cap = std::max<size_t>(words, std::max<size_t>(2 * st.cap, 4096));
-    if (st.host) hipHostFree(st.host);
+    if (st.host) (void)hipHostFree(st.host);
     st.host = st.dev = nullptr;
     st.cap = 0;
     hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&st.host), cap * sizeof(int32_t),
@@ -168,7 +168,7 @@ int ensure_dplan(pa_pool* p, size_t bytes) {
   const size_t cap = std::max(bytes, 2 * p->dplan_cap);
   hipError_t e = hipDeviceSynchronize();  // no launch may still read the old plan
   if (e != hipSuccess) return hip_err(e, "hipDeviceSynchronize");
-  if (p->dplan) hipFree(p->dplan);
+  if (p->dplan) (void)hipFree(p->dplan);
   p->dplan = nullptr;
   p->dplan_cap = 0;
   e = hipMalloc(&p->dplan, cap);
@@ -180,14 +180,14 @@ int ensure_dplan(pa_pool* p, size_t bytes) {
 void prof_begin(pa_pool* p, int which, hipStream_t s, ProfEvent* ev) {
   if (!p->prof) return;
   ev->which = which;
-  hipEventCreate(&ev->start);
-  hipEventCreate(&ev->stop);
-  hipEventRecord(ev->start, s);
+  (void)hipEventCreate(&ev->start);
+  (void)hipEventCreate(&ev->stop);
+  (void)hipEventRecord(ev->start, s);
 }
 
 void prof_end(pa_pool* p, hipStream_t s, ProfEvent* ev) {
   if (!p->prof) return;
-  hipEventRecord(ev->stop, s);
+  (void)hipEventRecord(ev->stop, s);
   p->prof_events.push_back(*ev);
 }
 
@@ -316,7 +316,7 @@ void make_plan(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, int rows, 
   std::vector<int> merge_of(n_seq, -1);
   for (size_t m = 0; m < p->merges.size(); ++m) merge_of[p->merges[m].q_row] = static_cast<int>(m);
   const auto& pairs = p->pre_scratch;  // (group key, batch index) sorted, prefix sequences only
-  const int rpw = pa::prefix_rows_per_unit(p->head_dim);
+  const int rpw = pa::prefix_rows_per_unit(p->dtype, p->head_dim);
   for (size_t a = 0; a < pairs.size();) {
     size_t b = a;
     while (b < pairs.size() && pairs[b].first == pairs[a].first) ++b;
@@ -395,8 +395,8 @@ void find_prefix_groups(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, i
 // 1,920 waves and 88 us.)
 int prefix_partition(const pa_pool* p, int pt0, int rows) {
   if (p->pre_groups.empty()) return pt0;
-  const int64_t rpw = pa::prefix_rows_per_unit(p->head_dim);
-  const int64_t resident = static_cast<int64_t>(p->num_cus) * pa::prefix_units_per_cu(p->head_dim);
+  const int64_t rpw = pa::prefix_rows_per_unit(p->dtype, p->head_dim);
+  const int64_t resident = static_cast<int64_t>(p->num_cus) * pa::prefix_units_per_cu(p->dtype, p->head_dim);
   auto waves = [&](int pt) {  // workgroups of the pass
     int64_t w = 0;
     for (const PrefixGroup& g : p->pre_groups)
@@ -425,7 +425,7 @@ int ensure_merge_ctr(pa_pool* p, size_t n) {
   const size_t cap = std::max(n, 2 * p->merge_ctr_cap);
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) return hip_err(e, "hipDeviceSynchronize");
-  if (p->merge_ctr) hipFree(p->merge_ctr);
+  if (p->merge_ctr) (void)hipFree(p->merge_ctr);
   p->merge_ctr = nullptr;
   p->merge_ctr_cap = 0;
   e = hipMalloc(&p->merge_ctr, cap * sizeof(unsigned));
@@ -790,18 +790,18 @@ int pa_create_pool(pa_pool** out, int num_blocks, int block_size, int num_kv_hea
 int pa_destroy_pool(pa_pool* p) {
   if (!p) return PA_OK;
   for (Stage& st : p->stage) {
-    if (st.pending) hipEventSynchronize(st.done);
-    if (st.done) hipEventDestroy(st.done);
-    if (st.host) hipHostFree(st.host);
+    if (st.pending) (void)hipEventSynchronize(st.done);
+    if (st.done) (void)hipEventDestroy(st.done);
+    if (st.host) (void)hipHostFree(st.host);
   }
   for (ProfEvent& ev : p->prof_events) {
-    hipEventDestroy(ev.start);
-    hipEventDestroy(ev.stop);
+    (void)hipEventDestroy(ev.start);
+    (void)hipEventDestroy(ev.stop);
   }
-  if (p->dplan || p->merge_ctr || p->kv_scale) hipDeviceSynchronize();
-  if (p->dplan) hipFree(p->dplan);
-  if (p->merge_ctr) hipFree(p->merge_ctr);
-  if (p->kv_scale) hipFree(p->kv_scale);
+  if (p->dplan || p->merge_ctr || p->kv_scale) (void)hipDeviceSynchronize();
+  if (p->dplan) (void)hipFree(p->dplan);
+  if (p->merge_ctr) (void)hipFree(p->merge_ctr);
+  if (p->kv_scale) (void)hipFree(p->kv_scale);
   delete p;
   return PA_OK;
 }
@@ -1137,8 +1137,8 @@ int pa_profile_read(pa_pool* p, int which, double* total_ms, int64_t* launches) 
     if (e != hipSuccess) return hip_err(e, "hipEventElapsedTime");
     p->prof_ms[ev.which] += ms;
     p->prof_n[ev.which] += 1;
-    hipEventDestroy(ev.start);
-    hipEventDestroy(ev.stop);
+    (void)hipEventDestroy(ev.start);
+    (void)hipEventDestroy(ev.stop);
   }
   p->prof_events.clear();
   if (total_ms) *total_ms = p->prof_ms[which];
