@@ -312,7 +312,8 @@ struct Range {
 __device__ inline Range resolve(const AttnParams& p, const Unit& u, int n_raw) {
   Range r;
   r.n = min(__builtin_amdgcn_readfirstlane(n_raw), p.max_blocks * kBlk);  // bounded by the table row
-  r.tok_end = u.nparts > 1 ? min(r.n, u.tok_begin + p.part_tokens) : r.n;
+  // a partition covers part_tokens tokens; the last one runs to the end
+  r.tok_end = (u.nparts > 1 && u.part < u.nparts - 1) ? min(r.n, u.tok_begin + p.part_tokens) : r.n;
   // causal: no row of the unit sees past the last row's position
   r.tok_end = min(r.tok_end, r.n - p.k_draft + u.clip_row / p.group + 1);
   return r;
@@ -1341,7 +1342,7 @@ void prefix_kernel(AttnParams p) {
   u.n_raw = pu.prefix_tokens;
   u.part = pu.part;
   u.tok_begin = pu.part * p.part_tokens;
-  u.nparts = 2;  // a partition: tokens [tok_begin, min(prefix, tok_begin + part_tokens))
+  u.nparts = 1 << 30;  // a partition never the last: tokens [tok_begin, min(prefix, tok_begin + part_tokens))
   u.slot_base = 0;
   u.pre_row0 = row0;
   u.pre_member0 = pu.member0;

@@ -250,12 +250,19 @@ int rows_limit(const pa_pool* p) { return pa::max_rows_for_head_dim(p->head_dim)
 
 // Partitions per sequence for partition length pt (0 = no split); returns the
 // number of partial slots (kv heads x partitions of every split sequence).
-int64_t count_parts(pa_pool* p, int n_seq, int pt) {
+// Partition q covers [q pt, (q + 1) pt) except the last, which runs to the
+// end of the sequence.  For calls of at most one 16-row tile (merged inside
+// the attention launch) the last partition absorbs a remainder of up to
+// pt / 4 tokens, so no partition is a handful of tokens whose merge lands at
+// the end of the launch (measured on MI355X: 70B-like decode 53.9 -> 53.4 us;
+// for verify's 20-row units the longer last partitions cost 4 %).
+int64_t count_parts(pa_pool* p, int n_seq, int pt, int rows) {
   p->parts.resize(n_seq);
   int64_t slots = 0;
+  const int slack = rows <= 16 ? pt / 4 : 0;
   for (int i = 0; i < n_seq; ++i) {
     const int n = p->lens[i];
-    p->parts[i] = (pt > 0 && n > pt) ? (n + pt - 1) / pt : 1;
+    p->parts[i] = (pt > 0 && n > pt + slack) ? (n - slack + pt - 1) / pt : 1;
     if (p->parts[i] > 1) slots += static_cast<int64_t>(p->parts[i]) * p->hkv;
   }
   return slots;
@@ -289,7 +296,8 @@ void make_plan(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, int rows, 
         continue;
       }
       for (int q = q0; q < parts; ++q) {
-        const int len = std::max(0, std::min({n, (q + 1) * pt, visible}) - q * pt);
+        const int end = q == parts - 1 ? n : (q + 1) * pt;  // the last partition runs to the end
+        const int len = std::max(0, std::min(end, visible) - q * pt);
         const pa::WorkUnit u{i, seq_ids[i], q, parts, base, row0, merge, parts - q0};
         if (len == pt)
           units.push_back(u);
@@ -370,7 +378,10 @@ void find_prefix_groups(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, i
         blocks = j;
       }
       const int shared = std::min(blocks * pa::kBlock, limit);
-      const int q_parts = shared / pt;
+      // whole partitions only, never a member's last one (it runs to the
+      // member's end, past the shared blocks)
+      int q_parts = shared / pt;
+      for (size_t k = a; k < b; ++k) q_parts = std::min(q_parts, p->parts[pairs[k].second] - 1);
       if (q_parts > 0) {
         p->pre_groups.push_back({shared, static_cast<int>(b - a)});
         for (size_t k = a; k < b; ++k) {
@@ -530,13 +541,13 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   int64_t slots;
   if (pt == 0) {
     pt = default_partition(rows);
-    slots = count_parts(p, n_seq, pt);
+    slots = count_parts(p, n_seq, pt, rows);
     if (slots && (!workspace || plan_ws_bytes(p, slots, rows) > ws_bytes)) {
       pt = 0;  // the workspace cannot hold the split: run unsplit
-      slots = count_parts(p, n_seq, 0);
+      slots = count_parts(p, n_seq, 0, rows);
     }
   } else {
-    slots = count_parts(p, n_seq, pt);
+    slots = count_parts(p, n_seq, pt, rows);
     if (slots && (!workspace || plan_ws_bytes(p, slots, rows) > ws_bytes))
       return set_err(PA_ERR_INVALID, "workspace too small for this partition size (see pa_workspace_size)");
   }
@@ -578,7 +589,7 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
     const int best = prefix_partition(p, pt, rows);
     if (best != pt) {
       pt = best;
-      slots = count_parts(p, n_seq, pt);
+      slots = count_parts(p, n_seq, pt, rows);
       find_prefix_groups(p, seq_ids, n_seq, pt, k_draft);
     }
   }
