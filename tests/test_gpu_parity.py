@@ -408,6 +408,27 @@ def test_shared_prefix_pass(prefix_len, k_draft, dtype):
     assert_close(b, lb, ro, rl, dtype, "private copies")
 
 
+def test_shared_prefix_forks_with_unsplit_members():
+    """Decode over six forks of a 530-token prefix at 512-token partitions:
+    members up to 640 tokens run unsplit (their last partition absorbs the
+    remainder), so no whole partition is split in every member and the
+    shared-prefix launch must not run; outputs match the oracle."""
+    w = make_custom(lengths=[10, 60, 100, 30, 200, 5], mode="append_decode", num_q_heads=16, num_kv_heads=4,
+                    head_dim=128, dtype="bf16", seed=41, prefix_len=530)
+    pair = Pair(w)
+    pair.fill()
+    pair.append_step_rows()
+    seqs = list(range(w.batch))
+    pair.gpu.profile_enable(True)
+    out, lse = _decode(pair, seqs, w.q, w.scale, pt=512)
+    torch.cuda.synchronize()
+    _, n_prefix = pair.gpu.profile_read(3)
+    pair.gpu.profile_enable(False)
+    assert n_prefix == 0, "a shared-prefix launch ran over unsplit members"
+    ro, rl = oracle_decode(pair, seqs, w.q, w.scale)
+    assert_close(out, lse, ro, rl, "bf16", "forks with unsplit members")
+
+
 def test_shared_prefix_pass_fused_append_decode():
     """Decode step of eight forks of a 1,536-token prefix as one
     pa_append_attend call: shared-prefix launch, then the fused append +
