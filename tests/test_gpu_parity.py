@@ -408,6 +408,24 @@ def test_shared_prefix_pass(prefix_len, k_draft, dtype):
     assert_close(b, lb, ro, rl, dtype, "private copies")
 
 
+@pytest.mark.parametrize("pt,lengths", [(512, [640, 641, 1152, 1153, 1025, 1]), (256, [320, 321, 576, 577, 257, 64])])
+def test_last_partition_absorbs_remainder_boundaries(pt, lengths):
+    """Lengths at and just past the point where a sequence's last partition
+    stops absorbing the remainder (a quarter partition): 640 tokens is one
+    unit at 512-token partitions, 641 is 512 + 129, 1152 is 512 + 640, 1153
+    is 512 + 512 + 129.  Decode, merged inside the launch, against the oracle."""
+    w = make_custom(lengths=[n - 1 for n in lengths], mode="append_decode", num_q_heads=16, num_kv_heads=4,
+                    head_dim=128, dtype="bf16", seed=42 + pt)
+    pair = Pair(w)
+    pair.fill()
+    pair.append_step_rows()
+    seqs = list(range(w.batch))
+    out, lse = _decode(pair, seqs, w.q, w.scale, pt=pt)
+    torch.cuda.synchronize()
+    ro, rl = oracle_decode(pair, seqs, w.q, w.scale)
+    assert_close(out, lse, ro, rl, "bf16", f"absorbed remainders pt={pt}")
+
+
 def test_shared_prefix_forks_with_unsplit_members():
     """Decode over six forks of a 530-token prefix at 512-token partitions:
     members up to 640 tokens run unsplit (their last partition absorbs the
