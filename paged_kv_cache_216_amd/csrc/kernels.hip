@@ -6,10 +6,21 @@
 //  attn_kernel       decode / speculative-verify attention over the block table:
 //                    one 64-lane wave per (sequence, partition, key/value head);
 //                    QK^T and PV on the matrix cores, online softmax in fp32.
+//                    Short splits (one row tile, few partitions) are merged by
+//                    the wave that finishes a sequence's last partition, with
+//                    device-scope stores and loads of the partials only.
+//  attn_append_kernel  the append work and attn_kernel in one launch: the
+//                    attention takes the rows this launch appends from k_new /
+//                    v_new instead of the pool.
+//  tile_kernel       many query rows per (sequence, kv head) -- chunked prefill,
+//                    long verifies: four waves share each pair of blocks through
+//                    an LDS ring filled by buffer loads with an LDS destination.
+//  prefix_kernel     the partitions of a prefix shared by copy-on-write forks,
+//                    once for the query rows of all of them.
 //  merge_kernel      exact log-sum-exp merge of the partitions of split
-//                    contexts (a separate launch: on MI355X each XCD has its
-//                    own L2, so merging inside the attention launch would need
-//                    device-scope write-back/invalidate fences per partition).
+//                    contexts, as a separate launch for long splits (each XCD
+//                    has its own L2, so merging many partitions inside the
+//                    attention launch would keep one wave busy after the rest).
 //
 // The pages describe the method (16-token blocks reached through a table inside
 // the attention kernel: "PagedAttention, décodage spéculatif, MoE et Blackwell",

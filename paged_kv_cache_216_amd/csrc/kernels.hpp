@@ -151,8 +151,8 @@ int append_blocks64(const AppendParams& p);
 // Query rows one single-wave attention unit takes at most, for a head dim.
 int max_rows_for_head_dim(int head_dim);
 // Query rows per unit for a call with `rows` rows per kv head: all of them when
-// one wave takes them; else a multi-wave workgroup's tile (16-bit pools) or a
-// single wave's (fp32 and E4M3 pools).
+// one wave takes them; else a multi-wave workgroup's tile (16-bit and E4M3
+// pools) or a single wave's (fp32 pools).
 int tile_rows_for_call(int dtype, int head_dim, int rows);
 
 }  // namespace pa
