@@ -68,8 +68,10 @@ __host__ __device__ inline AppendGrid append_grid(const AppendParams& p, int nth
 
 // Workgroup `b` (of nthreads threads) of the append work.  Table and length
 // updates, copies of the filled slots of shared blocks (rows [0, off) only, so
-// they never overlap the slots this call writes), and one 16-byte chunk of a
-// new row per thread.
+// they never overlap the slots the copying sequence writes; when another
+// sequence of the call writes into a copy's source block, the host issues the
+// copies in a launch of their own first), and one 16-byte chunk of a new row
+// per thread.
 // E4M3 code of a float: clamp to the largest finite magnitude (448), then
 // round to nearest, ties to even (the conversion instruction's rounding).
 __device__ inline uint32_t fp8_pack4(float a, float b, float c, float d) {

@@ -106,6 +106,7 @@ struct pa_pool {
   pa::BlockPool::Dirty dirty;
   std::vector<int32_t> slots;
   std::vector<pa::CowCopy> cows;
+  std::vector<int32_t> cow_src;  // sorted source blocks of this call's copies
   std::vector<pa::WorkUnit> units;
   std::vector<std::pair<int, pa::WorkUnit>> tail_units;  // (tokens the unit reads, unit)
   std::vector<pa::MergeUnit> merges;
@@ -468,8 +469,28 @@ int flush_dirty(pa_pool* p, hipStream_t stream) {
   return st ? release_stage(st, stream) : PA_OK;
 }
 
+// Whether a copy-on-write copy of this call reads a block that the same call
+// also writes rows into.  That happens when a longer sharer copies a shared
+// tail block and drops its reference, and a shorter sharer served later in the
+// call then holds the block alone and writes into it directly: the copy must
+// see the slots as they were before the call (the host model serves the
+// sequences one after the other), but the workgroups of one launch run in no
+// particular order.
+bool copy_source_written(pa_pool* p) {
+  if (p->cows.empty()) return false;
+  std::vector<int32_t>& src = p->cow_src;
+  src.clear();
+  for (const pa::CowCopy& c : p->cows) src.push_back(c.src);
+  std::sort(src.begin(), src.end());
+  for (int32_t s : p->slots)
+    if (std::binary_search(src.begin(), src.end(), s / pa::kBlock)) return true;
+  return false;
+}
+
 // Host bookkeeping for an append is done and its dirty set taken; enqueue its
-// kernel (table / length updates, copies, row scatter).
+// kernel (table / length updates, copies, row scatter).  When a copy's source
+// block is also written by this call, the copies run in a launch of their own
+// before the scatter (stream order makes the copies land first).
 int launch_append_call(pa_pool* p, const void* k_new, const void* v_new, hipStream_t stream) {
   p->meta.clear();
   pa::AppendParams ap = base_append(p);
@@ -486,13 +507,25 @@ int launch_append_call(pa_pool* p, const void* k_new, const void* v_new, hipStre
   ap.v_new = v_new;
   ap.n_cow = static_cast<int>(p->cows.size());
   ap.n_rows = static_cast<int>(p->slots.size());
+  const bool copies_first = copy_source_written(p);
   Stage* st = nullptr;
   int rc = meta_submit(p, &ap.ext, &st);
   if (rc != PA_OK) return rc;
   ProfEvent ev{};
   prof_begin(p, 2, stream, &ev);
-  hipError_t e = pa::launch_append(ap, &p->inline_meta, stream);
-  if (e != hipSuccess) return hip_err(e, "append kernel");
+  if (copies_first) {
+    // table / length updates and the copies, then the rows alone
+    pa::AppendParams first = ap, rows = ap;
+    first.n_rows = 0;
+    rows.n_tab = rows.n_len = rows.n_cow = 0;
+    hipError_t e = pa::launch_append(first, &p->inline_meta, stream);
+    if (e != hipSuccess) return hip_err(e, "append kernel (copy-on-write copies)");
+    e = pa::launch_append(rows, &p->inline_meta, stream);
+    if (e != hipSuccess) return hip_err(e, "append kernel");
+  } else {
+    hipError_t e = pa::launch_append(ap, &p->inline_meta, stream);
+    if (e != hipSuccess) return hip_err(e, "append kernel");
+  }
   prof_end(p, stream, &ev);
   return st ? release_stage(st, stream) : PA_OK;
 }
