@@ -16,4 +16,5 @@ from .synth import (  # noqa: F401
     make_prefill,
     make_custom,
     by_name,
+    with_rising_scores,
 )

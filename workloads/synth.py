@@ -284,3 +284,74 @@ def by_name(name: str, **kw) -> Workload:
         "long": make_long, "verify": make_verify, "prefill": make_prefill,
     }
     return table[name](**kw)
+
+
+# ---- inputs whose scores grow along the sequence -----------------------------
+
+def _storage_to_f32(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored values as float32 (bf16 bit patterns widened, f16 / f32 cast)."""
+    if dtype == "bf16":
+        return (np.asarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return np.asarray(bits).astype(np.float32)
+
+
+def with_rising_scores(w: Workload, every: int, offsets=(40, 100), gains=(1.0, 2.5), v_gain: float = 0.5,
+                       query_head: int = 0, new_row_gain: Optional[float] = None) -> Workload:
+    """A copy of ``w`` whose key rows make some query rows' largest score grow
+    well after the start of every ``every``-token span of each sequence.
+
+    At logical position ``b + offsets[j]`` (b a multiple of ``every``, the
+    position inside the sequence: shared prefix, then private rows, then the
+    appended rows) the key row of every kv head is set to ``gains[j]`` times
+    the sequence's first query of head ``kvh * G + query_head``; the spans of
+    the shared prefix take sequence 0's query.  Every value row is multiplied
+    by ``v_gain`` so that outputs stay well inside the output type's range.
+    With ``new_row_gain``, the last appended row of each sequence gets that
+    gain instead (a rise at the very end of the sequence).  All new values are
+    rounded to the storage type as the generator does.
+    """
+    import copy
+
+    out = copy.deepcopy(w)
+    g = w.num_q_heads // w.num_kv_heads
+    d = w.dtype
+    qf = _storage_to_f32(w.q, d)  # [B, K, Hq, D]
+
+    def plant(rows: np.ndarray, start: int, seq: int) -> np.ndarray:
+        """rows [n, Hkv, D] at logical positions start .. start + n - 1."""
+        if rows is None or rows.shape[0] == 0:
+            return rows
+        f = _storage_to_f32(rows, d).copy()
+        n = f.shape[0]
+        for b in range(0, start + n, every):
+            for off, gain in zip(offsets, gains):
+                pos = b + off
+                if start <= pos < start + n and off < every:
+                    for kvh in range(w.num_kv_heads):
+                        f[pos - start, kvh] = np.float32(gain) * qf[seq, 0, kvh * g + query_head]
+        return _to_storage(f, d)
+
+    def shrink(rows: np.ndarray) -> np.ndarray:
+        if rows is None or rows.shape[0] == 0:
+            return rows
+        return _to_storage(_storage_to_f32(rows, d) * np.float32(v_gain), d)
+
+    if w.prefix_len:
+        out.prefix_k = plant(w.prefix_k, 0, 0)
+        out.prefix_v = shrink(w.prefix_v)
+    for s in range(w.batch):
+        out.k_rows[s] = plant(w.k_rows[s], w.prefix_len, s)
+        out.v_rows[s] = shrink(w.v_rows[s])
+    if w.new_k is not None:
+        nk, nv = out.new_k.copy(), out.new_v.copy()
+        for s in range(w.batch):
+            nk[s] = plant(w.new_k[s], w.prefix_len + int(w.lengths[s]), s)
+            nv[s] = shrink(w.new_v[s])
+            if new_row_gain is not None:
+                f = _storage_to_f32(nk[s], d).copy()
+                for kvh in range(w.num_kv_heads):
+                    f[-1, kvh] = np.float32(new_row_gain) * qf[s, 0, kvh * g + query_head]
+                nk[s] = _to_storage(f, d)
+        out.new_k, out.new_v = nk, nv
+    out.name = w.name + "_rising"
+    return out
