@@ -170,12 +170,13 @@ class PoolModel:
         self.lens[seq] = t + 1
 
     @staticmethod
-    def _quantize(row_bf16: np.ndarray, scale: np.ndarray) -> np.ndarray:
-        """E4M3 codes of one [Hkv, D] bf16 row: E4M3(x * (1 / scale[h]))."""
-        from .fp8 import encode
+    def _quantize(row_bf16: np.ndarray, scale: np.ndarray, bulk: bool = False) -> np.ndarray:
+        """E4M3 codes of bf16 rows [..., Hkv, D]: E4M3(x * (1 / scale[h])).
+        ``bulk`` takes the search encoder (the same codes, for whole caches)."""
+        from .fp8 import encode, encode_by_search
         x = (as_bits(row_bf16, "bf16").astype(np.uint32) << np.uint32(16)).view(np.float32)
         inv = (np.float32(1.0) / scale.astype(np.float32)).astype(np.float32)
-        return encode((x * inv[:, None]).astype(np.float32))
+        return (encode_by_search if bulk else encode)((x * inv[:, None]).astype(np.float32))
 
     def append(self, seq_ids, n_tok, k_rows=None, v_rows=None) -> None:
         """Append n_tok[i] rows to seq_ids[i]; rows are packed in call order

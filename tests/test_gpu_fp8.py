@@ -194,25 +194,34 @@ def test_fp8_scale_calls_rejected():
             c.set_kv_scales([1.0, 1.0], bad)
 
 
-def test_full_highbatch_fp8_sampled():
-    """Batch 256 at the full size (log-normal lengths, 32 q / 8 kv heads):
-    sampled sequences against the oracle over their own rows quantized by the
-    oracle's encoder."""
+def test_full_highbatch_fp8_step():
+    """Batch 256 at the full size (log-normal lengths, 32 q / 8 kv heads) on
+    E4M3 pools, the step the bench times: one pa_append_attend call (fused
+    append + decode, in-launch merge).  Every sequence against the oracle over
+    its own rows quantized by the oracle's encoder; tables bit-exact."""
     w = make_highbatch()
-    _say("full highbatch fp8: fill")
+    _say("full highbatch fp8 step: fill")
     ks, vs = _scales(w.num_kv_heads)
     pair = Pair(w, track_data=False, cache_dtype="fp8", kv_scales=(ks, vs))
     pair.fill()
-    pair.append_step_rows()
-    pair.check_tables()
     seqs = list(range(w.batch))
-    out, lse = _attend(pair, seqs, w.q)
+    nk = to_torch(w.new_k.reshape(-1, w.num_kv_heads, w.head_dim), "bf16")
+    nv = to_torch(w.new_v.reshape(-1, w.num_kv_heads, w.head_dim), "bf16")
+    ws = pair.gpu.make_workspace(w.batch, w.num_q_heads, int(w.final_lengths().max()))
+    ws.fill_(float("nan"))
+    pair.gpu.profile_enable(True)
+    out, lse = pair.gpu.append_attend(seqs, nk, nv, to_torch(w.q, "bf16").contiguous(), w.scale, workspace=ws)
     torch.cuda.synchronize()
-    for s in (0, int(np.argmax(w.lengths)), 255):
-        _say(f"full highbatch fp8: oracle on {s}")
+    assert pair.gpu.profile_read(2)[1] == 0, "the append ran as a launch of its own"
+    pair.gpu.profile_enable(False)
+    pair.model.append(seqs, [1] * w.batch)
+    pair.check_tables()
+    o_all, l_all = out.float().cpu(), lse.cpu()
+    _say("full highbatch fp8 step: oracle on all 256 sequences")
+    for s in seqs:
         k = np.concatenate([w.k_rows[s], w.new_k[s]])
         v = np.concatenate([w.v_rows[s], w.new_v[s]])
-        kc = fp8_decode(PoolModel._quantize(k, ks)) * ks.astype(np.float64)[None, :, None]
-        vc = fp8_decode(PoolModel._quantize(v, vs)) * vs.astype(np.float64)[None, :, None]
+        kc = fp8_decode(PoolModel._quantize(k, ks, bulk=True)) * ks.astype(np.float64)[None, :, None]
+        vc = fp8_decode(PoolModel._quantize(v, vs, bulk=True)) * vs.astype(np.float64)[None, :, None]
         ro, rl = A.decode(kc, vc, to_f64(w.q[s].reshape(w.num_q_heads, w.head_dim), "bf16"), w.scale)
-        assert_close(out[s:s + 1], lse[s:s + 1], ro[None, None], rl[None, None], "fp8", f"highbatch fp8 seq {s}")
+        assert_close(o_all[s:s + 1], l_all[s:s + 1], ro[None, None], rl[None, None], "fp8", f"highbatch fp8 seq {s}")

@@ -270,22 +270,36 @@ def test_nomem_and_invalid_calls_change_nothing():
 
 
 # ---------------------------------------------------------------------------
-# full-size workloads, sampled outputs checked one sequence at a time
-def _sampled(pair, w, out, lse, samples, k_draft=1):
-    for s in samples:
-        if w.prefix_len:
-            k = np.concatenate([w.prefix_k, w.k_rows[s]] + ([w.new_k[s]] if w.new_k is not None else []))
-            v = np.concatenate([w.prefix_v, w.v_rows[s]] + ([w.new_v[s]] if w.new_v is not None else []))
-        elif w.mode == "append_decode":
-            k = np.concatenate([w.k_rows[s], w.new_k[s]])
-            v = np.concatenate([w.v_rows[s], w.new_v[s]])
-        else:
-            k, v = w.k_rows[s], w.v_rows[s]
+# full-size workloads: every sequence checked against the oracle over its own
+# logical rows (prefix, private rows, appended rows)
+def _logical_rows(w, s):
+    parts_k, parts_v = [], []
+    if w.prefix_len:
+        parts_k.append(w.prefix_k)
+        parts_v.append(w.prefix_v)
+    parts_k.append(w.k_rows[s])
+    parts_v.append(w.v_rows[s])
+    if w.new_k is not None and w.mode in ("append_decode", "verify"):
+        parts_k.append(w.new_k[s])
+        parts_v.append(w.new_v[s])
+    return np.concatenate(parts_k), np.concatenate(parts_v)
+
+
+def _check_all(w, out, lse, k_draft=1):
+    o_all = out.detach().float().cpu()
+    l_all = lse.detach().cpu()
+    worst = 0.0
+    for s in range(w.batch):
+        k, v = _logical_rows(w, s)
         ro, rl = contiguous_reference(k, v, w.q[s], w.scale, w.dtype, k_draft)
-        assert_close(out[s:s + 1], lse[s:s + 1], ro[None], rl[None], w.dtype, f"{w.name} seq {s}")
+        worst = max(worst, assert_close(o_all[s:s + 1], l_all[s:s + 1], ro[None], rl[None], w.dtype,
+                                        f"{w.name} seq {s}"))
+    _say(f"full {w.name}: all {w.batch} sequences within tolerance (max err {worst:.2e})")
 
 
-def _full(w, samples):
+def _full(w):
+    """Fill, append the step's rows, then one attention call at the library's
+    partition choice: every output row and lse against the oracle."""
     _say(f"full {w.name}: fill")
     pair = Pair(w, track_data=False)
     pair.fill()
@@ -295,26 +309,61 @@ def _full(w, samples):
     seqs = list(range(w.batch))
     out, lse = _decode(pair, seqs, w.q, w.scale, k_draft=w.k_draft)
     torch.cuda.synchronize()
-    _say(f"full {w.name}: oracle on {samples}")
-    _sampled(pair, w, out, lse, samples, w.k_draft)
+    _say(f"full {w.name}: oracle on all {w.batch} sequences")
+    _check_all(w, out, lse, w.k_draft)
+    return pair
+
+
+def _full_step(w):
+    """The step bench.py times: pa_append_attend (append the step's rows and
+    attend, one launch when possible) at the library's partition choice with a
+    workspace sized as the bench sizes it.  Every output row and lse against
+    the oracle, tables bit-exact."""
+    _say(f"full step {w.name}: fill")
+    pair = Pair(w, track_data=False)
+    pair.fill()
+    pair.check_tables()
+    seqs = list(range(w.batch))
+    t = w.new_k.shape[1]
+    nk = to_torch(w.new_k.reshape(-1, w.num_kv_heads, w.head_dim), w.dtype)
+    nv = to_torch(w.new_v.reshape(-1, w.num_kv_heads, w.head_dim), w.dtype)
+    q = to_torch(w.q, w.dtype).contiguous()
+    ws = pair.gpu.make_workspace(w.batch, w.num_q_heads, int(w.final_lengths().max()), k_draft=t)
+    ws.fill_(float("nan"))
+    pair.gpu.profile_enable(True)
+    out, lse = pair.gpu.append_attend(seqs, nk, nv, q, w.scale, workspace=ws)
+    torch.cuda.synchronize()
+    n_append = pair.gpu.profile_read(2)[1]
+    pair.gpu.profile_enable(False)
+    assert n_append == 0, "the append ran as a launch of its own"
+    pair.model.append(seqs, [t] * w.batch)
+    pair.check_tables()
+    _say(f"full step {w.name}: oracle on all {w.batch} sequences")
+    _check_all(w, out, lse, t)
     return pair
 
 
 def test_full_gqa70b():
-    _full(make_gqa70b(), [0, 7, 31])
+    _full(make_gqa70b())
 
 
 def test_full_highbatch():
-    w = make_highbatch()
-    _full(w, [0, int(np.argmax(w.lengths)), 255])
+    _full(make_highbatch())
 
 
 def test_full_long():
-    _full(make_long(), [0, 7])
+    _full(make_long())
 
 
-def test_full_verify():
-    pair = _full(make_verify(), [0, 17, 33, 50, 63])
+def test_full_highbatch_step():
+    """Batch 256, log-normal lengths: the fused append + decode launch with
+    the in-launch merge of split sequences, exactly as timed."""
+    pair = _full_step(make_highbatch())
+    pt, _ = pair.gpu.last_partition()
+    assert pt == 512, pt
+
+
+def _check_verify_partition(pair):
     # The library chose the partition: at the default 512 tokens the shared-
     # prefix pass would need 8 partitions x 40 row blocks x 8 kv heads = 2,560
     # workgroups, more than one round of the 8 per CU the device holds at
@@ -326,6 +375,16 @@ def test_full_verify():
     assert prefix_wgs == (4096 // pt) * 40 * 8, (pt, prefix_wgs)
     if 8 * 40 * 8 > resident:
         assert prefix_wgs <= resident, (pt, prefix_wgs, resident)
+
+
+def test_full_verify():
+    _check_verify_partition(_full(make_verify()))
+
+
+def test_full_verify_step():
+    """64 forks of a 4,096-token prefix, 5 drafts appended and verified in one
+    pa_append_attend call: shared-prefix pass, fused append + attention, merge."""
+    _check_verify_partition(_full_step(make_verify()))
 
 
 def test_many_partitions_fused_merge_and_repeat():

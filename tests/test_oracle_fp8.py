@@ -98,3 +98,19 @@ def test_pool_model_stores_scaled_codes_and_gather_rescales():
     ks, vs = A.gather(m.kpool, m.vpool, m.table(0), 1, "fp8", (m.k_scale, m.v_scale))
     assert np.all(ks[0, 0] == 1.0) and np.all(ks[0, 1] == -3.0) and np.all(ks[0, 2] == 448.0)
     assert np.all(vs[0, 2] == 6.0)
+
+
+def test_search_encoder_equals_brute_force():
+    """encode_by_search gives the brute-force encoder's code for every finite
+    bf16 value, every midpoint between neighbouring codes (and a float32 ulp
+    either side), values past the clamp and random float32 inputs."""
+    from oracle.fp8 import _POS, encode_by_search
+
+    bits = np.arange(1 << 16, dtype=np.uint32) << np.uint32(16)
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    mids = ((_POS[1:] + _POS[:-1]) / 2).astype(np.float32)
+    near = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9))])
+    rnd = np.random.default_rng(5).standard_normal(200_000).astype(np.float32) * np.float32(40)
+    for arr in (x, near, -near, rnd, np.array([448.0, 449.0, 464.0, 1e30, -1e30, 0.0, -0.0], np.float32)):
+        assert np.array_equal(encode_by_search(arr), fp8.encode(arr))
