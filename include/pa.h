@@ -240,6 +240,25 @@ int pa_decode(pa_pool* pool, const int32_t* seq_ids, int n_seq, int num_q_heads,
               const void* q, void* out, float* lse, int partition_tokens, void* workspace,
               size_t ws_bytes, void* stream);
 
+/* pa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments and results as pa_decode (bitwise), without the workspace: the
+ * work plan, the in-launch merge counters and the split partials live in a
+ * fixed device array of 32 MiB per GPU, [0, 64 KiB) counters, [64 KiB,
+ * 1 MiB) plan, [1 MiB, 32 MiB) partials, that the library holds on every GPU
+ * it runs on until the process ends.  The call allocates nothing (no
+ * hipMalloc, no pinned staging, no profiling events) and copies nothing from
+ * the host: the plan and pending table updates travel in kernel arguments.
+ * partition_tokens = 0 splits only when the partials fit the array; an
+ * explicit partition whose partials do not fit, a plan past 960 KiB or more
+ * than 16,384 (split sequence, kv head) merge counters return PA_ERR_INVALID
+ * before any launch.  Every call on one GPU shares that GPU's array (it keeps
+ * the last call's contents; the counters a call uses are zeroed by the call):
+ * calls that overlap on one GPU -- on different streams, or from different
+ * pools on different streams -- race, and must be ordered by the caller. */
+int pa_decode_noalloc(pa_pool* pool, const int32_t* seq_ids, int n_seq, int num_q_heads, float scale,
+                      const void* q, void* out, float* lse, int partition_tokens, void* stream);
+
 /* Speculative verify: the last k_draft rows of each sequence are draft tokens
  * (already appended) and draft i (0-based) attends to positions
  * [0, length - k_draft + i], its own row included (P1 section 1 and P2

@@ -31,6 +31,8 @@ SIGNATURES = {
     "pa_append_kv": (c_int, [c_void_p, c_i32p, c_int, c_i32p, c_void_p, c_void_p, c_void_p]),
     "pa_decode": (c_int, [c_void_p, c_i32p, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p, c_int,
                           c_void_p, c_size_t, c_void_p]),
+    "pa_decode_noalloc": (c_int, [c_void_p, c_i32p, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p, c_int,
+                                  c_void_p]),
     "pa_verify": (c_int, [c_void_p, c_i32p, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p,
                           c_int, c_void_p, c_size_t, c_void_p]),
     "pa_swap_bytes": (c_int, [c_void_p, c_int, ctypes.POINTER(c_size_t)]),

@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpa.so")
-SOURCES = ["block_pool.cpp", "pa_api.cpp", "kernels.hip", "swap.hip"]
+SOURCES = ["block_pool.cpp", "pa_api.cpp", "kernels.hip", "swap.hip", "scratch.hip"]
 ARCH = "gfx950"
 
 

@@ -247,6 +247,22 @@ class PagedKVCache:
         n_seq, hq, d = q.shape
         return self._attend(seq_ids, 1, q, hq, scale, out, lse, want_lse, partition_tokens, workspace, stream)
 
+    def decode_noalloc(self, seq_ids, q: torch.Tensor, scale: float, out: torch.Tensor, lse: Optional[torch.Tensor],
+                       partition_tokens: int = 0, stream=None):
+        """pa_decode_noalloc: q, out [n_seq, Hq, D] and lse [n_seq, Hq] (or None)
+        are caller-allocated; the library's fixed device scratch holds the
+        plan and the split partials."""
+        if q.dtype != self.tdtype or not q.is_contiguous() or q.dim() != 3 or q.shape[-1] != self.d:
+            raise ValueError("q must be a contiguous [n_seq, Hq, D] tensor in the pool dtype")
+        if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+            raise ValueError("out must be a contiguous tensor shaped like q")
+        ids, n = abi.i32_array(seq_ids)
+        if n != q.shape[0]:
+            raise ValueError("one query set per sequence")
+        abi.check(self.lib.pa_decode_noalloc(self.handle, ids, n, q.shape[1], float(scale), _ptr(q), _ptr(out),
+                                             _ptr(lse), partition_tokens, _stream(stream)))
+        return out, lse
+
     def verify(self, seq_ids, q: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
                lse: Optional[torch.Tensor] = None, want_lse: bool = True, partition_tokens: int = 0,
                workspace: Optional[torch.Tensor] = None, stream=None):

@@ -23,6 +23,7 @@
 
 #include "block_pool.hpp"
 #include "kernels.hpp"
+#include "scratch.hpp"
 #include "swap.hpp"
 
 namespace {
@@ -84,6 +85,7 @@ struct pa_pool {
   int32_t* block_table = nullptr;
   int32_t* seq_len = nullptr;
   bool host_only = false;
+  char* scratch = nullptr;  // this device's fixed scratch (pa_decode_noalloc)
   int num_cus = 256;  // compute units of the pool's device
   int last_pt = 0, last_prefix_units = 0;  // of the last attention call
   // metadata ring
@@ -92,6 +94,7 @@ struct pa_pool {
   // cached attention plan in device memory: WorkUnits then MergeUnits
   void* dplan = nullptr;
   size_t dplan_cap = 0;  // bytes
+  bool dplan_stale = false;  // the host plan changed without an upload to dplan
   // E4M3 pools: [4][hkv] k_scale, v_scale, 1/k_scale, 1/v_scale (device; host copy)
   float* kv_scale = nullptr;
   std::vector<float> kv_scale_host;
@@ -487,6 +490,41 @@ bool copy_source_written(pa_pool* p) {
   return false;
 }
 
+// flush_dirty with every launch's metadata in its kernel arguments (no
+// staging buffer): as many update-only launches as the pending updates need.
+int flush_dirty_inline(pa_pool* p, hipStream_t stream) {
+  if (!p->bp.has_dirty()) return PA_OK;
+  p->bp.take_dirty(&p->dirty);
+  const pa::BlockPool::Dirty& d = p->dirty;
+  constexpr size_t kPer = (pa::kInlineWords - 16) / 2;  // (index, value) pairs per launch
+  size_t it = 0, il = 0;
+  while (it < d.table_idx.size() || il < d.len_seq.size()) {
+    const size_t nt = std::min(kPer, d.table_idx.size() - it);
+    const size_t nl = std::min(kPer - nt, d.len_seq.size() - il);
+    std::vector<int32_t>& w = p->meta;
+    w.clear();
+    pa::AppendParams ap = base_append(p);
+    ap.tab = 0;
+    for (size_t i = it; i < it + nt; ++i) {
+      w.push_back(d.table_idx[i]);
+      w.push_back(d.table_val[i]);
+    }
+    ap.lens = static_cast<int>(pad8(w));
+    for (size_t i = il; i < il + nl; ++i) {
+      w.push_back(d.len_seq[i]);
+      w.push_back(d.len_val[i]);
+    }
+    ap.n_tab = static_cast<int>(nt);
+    ap.n_len = static_cast<int>(nl);
+    std::memcpy(p->inline_meta.w, w.data(), w.size() * sizeof(int32_t));
+    hipError_t e = pa::launch_append(ap, &p->inline_meta, stream);
+    if (e != hipSuccess) return hip_err(e, "append kernel (table update)");
+    it += nt;
+    il += nl;
+  }
+  return PA_OK;
+}
+
 // Host bookkeeping for an append is done and its dirty set taken; enqueue its
 // kernel (table / length updates, copies, row scatter).  When a copy's source
 // block is also written by this call, the copies run in a launch of their own
@@ -538,11 +576,19 @@ struct AppendSpec {
 
 // Attention over the current lengths; with `app`, first append app->t_new rows
 // to every sequence, in the same launch when possible.
+// With `noalloc` (no append): the plan, the merge counters and the partials go
+// to the device's fixed scratch, all metadata travels in kernel arguments, and
+// nothing is allocated; sizes past the scratch are rejected.
 int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q_heads, float scale,
            const void* q, void* out, float* lse, int partition_tokens, void* workspace, size_t ws_bytes,
-           void* stream_v, const AppendSpec* app) {
+           void* stream_v, const AppendSpec* app, bool noalloc = false) {
   if (!p) return set_err(PA_ERR_INVALID, "pool is NULL");
   if (p->host_only) return set_err(PA_ERR_STATE, "host-only pool has no device memory");
+  if (noalloc) {
+    if (app || !p->scratch) return set_err(PA_ERR_STATE, "no device scratch for this pool");
+    workspace = p->scratch + pa::kScratchPartialOffset;
+    ws_bytes = pa::kScratchPartialBytes;
+  }
   if (n_seq < 0) return set_err(PA_ERR_INVALID, "n_seq < 0");
   if (k_draft < 1) return set_err(PA_ERR_INVALID, "k_draft must be >= 1");
   if (num_q_heads <= 0 || num_q_heads % p->hkv != 0)
@@ -582,7 +628,8 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   } else {
     slots = count_parts(p, n_seq, pt, rows);
     if (slots && (!workspace || plan_ws_bytes(p, slots, rows) > ws_bytes))
-      return set_err(PA_ERR_INVALID, "workspace too small for this partition size (see pa_workspace_size)");
+      return set_err(PA_ERR_INVALID, noalloc ? "split partials for this partition size exceed the fixed scratch"
+                                             : "workspace too small for this partition size (see pa_workspace_size)");
   }
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
 
@@ -611,7 +658,7 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
     }
   }
   if (!fused) {
-    int rc = flush_dirty(p, stream);
+    int rc = noalloc ? flush_dirty_inline(p, stream) : flush_dirty(p, stream);
     if (rc != PA_OK) return rc;
   }
 
@@ -638,31 +685,67 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   }
   if (key != p->plan_key) {
     make_plan(p, seq_ids, n_seq, pt, rows, group, k_draft);
-    const size_t w_units = 8 * p->units.size(), w_merges = 4 * p->merges.size();
-    const size_t w_pre = 8 * p->pre_units.size(), w_mem = 4 * p->pre_members.size();
-    const size_t plan_words = w_units + w_merges + w_pre + w_mem;
-    int rc = ensure_dplan(p, plan_words * sizeof(int32_t));
-    if (rc != PA_OK) return rc;
-    if (plan_words) {
-      Stage* pst = nullptr;
-      rc = acquire_stage(p, plan_words, &pst);
-      if (rc != PA_OK) return rc;
-      int32_t* h = pst->host;
-      std::memcpy(h, p->units.data(), w_units * sizeof(int32_t));
-      std::memcpy(h + w_units, p->merges.data(), w_merges * sizeof(int32_t));
-      std::memcpy(h + w_units + w_merges, p->pre_units.data(), w_pre * sizeof(int32_t));
-      std::memcpy(h + w_units + w_merges + w_pre, p->pre_members.data(), w_mem * sizeof(int32_t));
-      hipError_t e = hipMemcpyAsync(p->dplan, pst->host, plan_words * sizeof(int32_t), hipMemcpyHostToDevice, stream);
-      if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync(plan)");
-      rc = release_stage(pst, stream);
-      if (rc != PA_OK) return rc;
-    }
-    rc = ensure_merge_ctr(p, p->merges.size() * static_cast<size_t>(p->hkv));
-    if (rc != PA_OK) return rc;
     p->plan_key.swap(key);
     p->plan_units = static_cast<int>(p->units.size());
     p->plan_merges = static_cast<int>(p->merges.size());
     p->plan_pre_units = static_cast<int>(p->pre_units.size());
+    p->dplan_stale = true;
+  }
+  const size_t w_units = 8 * p->units.size(), w_merges = 4 * p->merges.size();
+  const size_t w_pre = 8 * p->pre_units.size(), w_mem = 4 * p->pre_members.size();
+  const size_t plan_words = w_units + w_merges + w_pre + w_mem;
+  auto plan_image = [&](int32_t* h) {
+    std::memcpy(h, p->units.data(), w_units * sizeof(int32_t));
+    std::memcpy(h + w_units, p->merges.data(), w_merges * sizeof(int32_t));
+    std::memcpy(h + w_units + w_merges, p->pre_units.data(), w_pre * sizeof(int32_t));
+    std::memcpy(h + w_units + w_merges + w_pre, p->pre_members.data(), w_mem * sizeof(int32_t));
+  };
+  const int32_t* dplan = nullptr;
+  unsigned* merge_ctr = nullptr;
+  if (noalloc) {
+    // the scratch is shared by every pool on the device: the plan goes in on
+    // every call, through kernel arguments, with the counters it uses zeroed
+    const size_t n_ctr = p->merges.size() * static_cast<size_t>(p->hkv);
+    if (plan_words * sizeof(int32_t) > pa::kScratchPlanBytes)
+      return set_err(PA_ERR_INVALID, "work plan exceeds the fixed scratch (too many sequences or partitions)");
+    if (n_ctr * sizeof(unsigned) > pa::kScratchCounterBytes)
+      return set_err(PA_ERR_INVALID, "merge counters exceed the fixed scratch (too many split sequences)");
+    int32_t* dst = reinterpret_cast<int32_t*>(p->scratch + pa::kScratchPlanOffset);
+    unsigned* ctr = reinterpret_cast<unsigned*>(p->scratch);
+    p->meta.resize(plan_words);
+    plan_image(p->meta.data());
+    size_t done = 0;
+    do {
+      const size_t n = std::min(plan_words - done, static_cast<size_t>(pa::kInlineWords));
+      std::memcpy(p->inline_meta.w, p->meta.data() + done, n * sizeof(int32_t));
+      hipError_t e = pa::launch_words(dst + done, p->inline_meta, static_cast<int>(n), ctr,
+                                      done == 0 ? static_cast<int>(n_ctr) : 0, stream);
+      if (e != hipSuccess) return hip_err(e, "scratch plan");
+      done += n;
+    } while (done < plan_words);
+    dplan = dst;
+    merge_ctr = ctr;
+  } else {
+    if (p->dplan_stale) {
+      int rc = ensure_dplan(p, plan_words * sizeof(int32_t));
+      if (rc != PA_OK) return rc;
+      if (plan_words) {
+        Stage* pst = nullptr;
+        rc = acquire_stage(p, plan_words, &pst);
+        if (rc != PA_OK) return rc;
+        plan_image(pst->host);
+        hipError_t e =
+            hipMemcpyAsync(p->dplan, pst->host, plan_words * sizeof(int32_t), hipMemcpyHostToDevice, stream);
+        if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync(plan)");
+        rc = release_stage(pst, stream);
+        if (rc != PA_OK) return rc;
+      }
+      rc = ensure_merge_ctr(p, p->merges.size() * static_cast<size_t>(p->hkv));
+      if (rc != PA_OK) return rc;
+      p->dplan_stale = false;
+    }
+    dplan = static_cast<const int32_t*>(p->dplan);
+    merge_ctr = p->merge_ctr;
   }
 
   pa::AttnParams ak{};
@@ -679,8 +762,7 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   float* ws = static_cast<float*>(workspace);
   ak.ws_acc = ws;
   ak.ws_ml = ws ? ws + static_cast<size_t>(slots) * rows * p->head_dim : nullptr;
-  ak.units = static_cast<const pa::WorkUnit*>(p->dplan);
-  const int32_t* dplan = static_cast<const int32_t*>(p->dplan);
+  ak.units = reinterpret_cast<const pa::WorkUnit*>(dplan);
   ak.merges = reinterpret_cast<const pa::MergeUnit*>(dplan + 8 * p->plan_units);
   ak.pre_units = reinterpret_cast<const pa::PrefixUnit*>(dplan + 8 * p->plan_units + 4 * p->plan_merges);
   ak.pre_members = reinterpret_cast<const pa::PrefixMember*>(dplan + 8 * p->plan_units + 4 * p->plan_merges +
@@ -700,7 +782,7 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   ak.app = base_append(p);
   // Short splits (few partitions, one row tile) are merged inside the
   // attention launch by the last partition to finish; others by merge_kernel.
-  ak.merge_ctr = p->merge_ctr;
+  ak.merge_ctr = merge_ctr;
   ak.kv_scale = p->kv_scale;
   ak.inline_merge = (p->dtype != PA_F32 && rows <= 16 && p->plan_max_parts <= pa::kInlineMergeParts &&
                      ws_bytes < (size_t{1} << 31)) ? 1 : 0;
@@ -726,24 +808,24 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   const pa::DType dt = static_cast<pa::DType>(p->dtype);
   if (ak.n_pre_units > 0) {
     ProfEvent ev{};
-    prof_begin(p, 3, stream, &ev);
+    if (!noalloc) prof_begin(p, 3, stream, &ev);
     hipError_t e = pa::launch_prefix(dt, ak, stream);
     if (e != hipSuccess) return hip_err(e, "shared-prefix kernel");
-    prof_end(p, stream, &ev);
+    if (!noalloc) prof_end(p, stream, &ev);
   }
   if (ak.n_units > 0 || fused) {
     ProfEvent ev{};
-    prof_begin(p, 0, stream, &ev);
+    if (!noalloc) prof_begin(p, 0, stream, &ev);
     hipError_t e = pa::launch_attention(dt, ak, &p->inline_meta, stream);
     if (e != hipSuccess) return hip_err(e, "attention kernel");
-    prof_end(p, stream, &ev);
+    if (!noalloc) prof_end(p, stream, &ev);
   }
   if (ak.n_merges > 0 && !ak.inline_merge) {
     ProfEvent ev{};
-    prof_begin(p, 1, stream, &ev);
+    if (!noalloc) prof_begin(p, 1, stream, &ev);
     hipError_t e = pa::launch_merge(dt, ak, stream);
     if (e != hipSuccess) return hip_err(e, "merge kernel");
-    prof_end(p, stream, &ev);
+    if (!noalloc) prof_end(p, stream, &ev);
   }
   p->last_pt = slots > 0 ? pt : 0;
   p->last_prefix_units = ak.n_pre_units * p->hkv;
@@ -807,6 +889,12 @@ int pa_create_pool(pa_pool** out, int num_blocks, int block_size, int num_kv_hea
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
       p->num_cus = cus;
+    // the device's fixed scratch (pa_decode_noalloc), looked up once per device
+    hipError_t se = pa::scratch_address(dev, &p->scratch);
+    if (se != hipSuccess) {
+      pa_destroy_pool(p);
+      return hip_err(se, "hipGetSymbolAddress(scratch)");
+    }
     for (Stage& st : p->stage) {
       hipError_t e = hipEventCreateWithFlags(&st.done, hipEventDisableTiming);
       if (e != hipSuccess) {
@@ -1047,6 +1135,12 @@ int pa_decode(pa_pool* p, const int32_t* seq_ids, int n_seq, int num_q_heads, fl
               size_t ws_bytes, void* stream) {
   return attend(p, seq_ids, n_seq, 1, num_q_heads, scale, q, out, lse, partition_tokens, workspace,
                 ws_bytes, stream, nullptr);
+}
+
+int pa_decode_noalloc(pa_pool* p, const int32_t* seq_ids, int n_seq, int num_q_heads, float scale, const void* q,
+                      void* out, float* lse, int partition_tokens, void* stream) {
+  return attend(p, seq_ids, n_seq, 1, num_q_heads, scale, q, out, lse, partition_tokens, nullptr, 0, stream,
+                nullptr, true);
 }
 
 int pa_verify(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q_heads, float scale,
