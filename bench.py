@@ -239,66 +239,91 @@ def describe(w) -> str:
     return d[w.name]
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(w, budget_s, cache_dtype, scales):
-    """The float64 oracle, single-threaded, on the first sequences of the same
-    workload until `budget_s` seconds of work; reported in the metric's unit."""
-    from threadpoolctl import threadpool_limits
+    """The float64 oracle as it stands, on the first sequences of the same
+    workload: first with one BLAS thread until about half of `budget_s`
+    seconds of work, then the same sample with the BLAS library's own thread
+    count (all the cores it uses).  Reported in the metric's unit."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import attention as A
     from oracle.allocator import PoolModel
 
     lens = step_lengths(w)
-    done_bytes, done_flops, elapsed, nseq, ntok = 0, 0, 0.0, 0, 0
+
+    def one(s):
+        m = PoolModel(w.num_blocks, w.num_kv_heads, w.head_dim, cache_dtype, 1, w.max_blocks_per_seq,
+                      free_order=w.free_order, kv_scales=scales)
+        m.alloc(0)
+        parts_k, parts_v = [], []
+        if w.prefix_len:
+            parts_k.append(w.prefix_k)
+            parts_v.append(w.prefix_v)
+        parts_k.append(w.k_rows[s])
+        parts_v.append(w.v_rows[s])
+        if w.new_k is not None and w.mode in ("append_decode", "verify"):
+            parts_k.append(w.new_k[s])
+            parts_v.append(w.new_v[s])
+        k, v = np.concatenate(parts_k), np.concatenate(parts_v)
+        t0 = time.perf_counter()
+        m.append([0], [k.shape[0]], k, v)
+        if w.k_draft == 1:
+            A.decode_from_pool(m.kpool, m.vpool, m.table(0), m.length(0), w.q[s, 0], w.scale, cache_dtype, scales)
+        else:
+            A.verify_from_pool(m.kpool, m.vpool, m.table(0), m.length(0), w.q[s], w.scale, cache_dtype, scales)
+        return time.perf_counter() - t0
+
+    sample, t1 = [], 0.0
     with threadpool_limits(limits=1):
         for s in range(w.batch):
-            m = PoolModel(w.num_blocks, w.num_kv_heads, w.head_dim, cache_dtype, 1, w.max_blocks_per_seq,
-                          free_order=w.free_order, kv_scales=scales)
-            m.alloc(0)
-            parts_k, parts_v = [], []
-            if w.prefix_len:
-                parts_k.append(w.prefix_k)
-                parts_v.append(w.prefix_v)
-            parts_k.append(w.k_rows[s])
-            parts_v.append(w.v_rows[s])
-            if w.new_k is not None and w.mode in ("append_decode", "verify"):
-                parts_k.append(w.new_k[s])
-                parts_v.append(w.new_v[s])
-            k, v = np.concatenate(parts_k), np.concatenate(parts_v)
-            t0 = time.perf_counter()
-            m.append([0], [k.shape[0]], k, v)
-            if w.k_draft == 1:
-                A.decode_from_pool(m.kpool, m.vpool, m.table(0), m.length(0), w.q[s, 0], w.scale, cache_dtype,
-                                   scales)
-            else:
-                A.verify_from_pool(m.kpool, m.vpool, m.table(0), m.length(0), w.q[s], w.scale, cache_dtype, scales)
-            elapsed += time.perf_counter() - t0
-            n = lens[s]
-            done_bytes += (n * w.num_kv_heads * w.head_dim * EB[cache_dtype] * 2
-                           + 2 * w.k_draft * w.num_q_heads * w.head_dim * EB[w.dtype] + math.ceil(n / 16) * 4 + 4)
-            done_flops += 4 * w.head_dim * w.num_q_heads * (w.k_draft * (n - w.k_draft + 1)
-                                                            + w.k_draft * (w.k_draft - 1) // 2)
-            nseq += 1
-            ntok += n
-            if elapsed >= budget_s:
+            t1 += one(s)
+            sample.append(s)
+            if t1 >= budget_s / 2:
                 break
+    threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    tn = sum(one(s) for s in sample)
+    done_bytes = done_flops = ntok = 0
+    for s in sample:
+        n = lens[s]
+        done_bytes += (n * w.num_kv_heads * w.head_dim * EB[cache_dtype] * 2
+                       + 2 * w.k_draft * w.num_q_heads * w.head_dim * EB[w.dtype] + math.ceil(n / 16) * 4 + 4)
+        done_flops += 4 * w.head_dim * w.num_q_heads * (w.k_draft * (n - w.k_draft + 1)
+                                                        + w.k_draft * (w.k_draft - 1) // 2)
+        ntok += n
     if is_prefill(w):
-        value, unit = done_flops / elapsed / 1e12, "TFLOP/s"
+        unit, work, scale = "TFLOP/s", done_flops, 1e12
     else:
-        value, unit = done_bytes / elapsed / 1e9, "GB/s"
+        unit, work, scale = "GB/s", done_bytes, 1e9
     return {
-        "value": round(value, 6), "unit": unit, "cores": 1, "kind": "oracle",
-        "sample": f"first {nseq} of {w.batch} sequences ({ntok} cached tokens): append into the float64 "
-                  f"oracle's pool model, then gather + softmax attention; one thread; {elapsed:.1f} s",
-        "cpu": platform.processor() or platform.machine(), "host_cpus": os.cpu_count(),
+        "value": round(work / tn / scale, 6), "unit": unit, "cores": threads, "kind": "oracle",
+        "sample": f"first {len(sample)} of {w.batch} sequences ({ntok} cached tokens): append into the float64 "
+                  f"oracle's pool model, then gather + softmax attention, per sequence in Python; "
+                  f"{tn:.1f} s with the BLAS library's {threads} threads, {t1:.1f} s with one",
+        "single_thread": {"value": round(work / t1 / scale, 6), "unit": unit, "cores": 1},
+        "cpu": cpu_model(), "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
     }
 
 
 def kernel_source_id() -> str:
-    """Hash of the kernel sources: counter figures recorded for other sources
-    no longer describe the kernel."""
+    """Hash of the kernel sources and of the host code that plans their
+    launches (partition choice, work units): counter figures recorded for
+    other sources no longer describe the kernels."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("kernels.hip", "kernels.hpp"):
+    for f in ("kernels.hip", "kernels.hpp", "pa_api.cpp"):
         with open(os.path.join(ROOT, "paged_kv_cache_216_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -486,9 +511,11 @@ def main():
         pct = {"p50": round(float(np.percentile(st, 50)), 2), "p90": round(float(np.percentile(st, 90)), 2),
                "p99": round(float(np.percentile(st, 99)), 2), "mean": round(float(st.mean()), 2)}
     pt_used, prefix_wgs = reps[0].cache.last_partition()
+    stats = reps[0].cache.last_call_stats()
     hbm_ref = None if args.no_profile_events else copy_reference()
-    dec_b = decode_bytes(w, EB[cd])
-    app_b = append_bytes(w, EB[cd])
+    kv_eb, e = EB[cd], EB[w.dtype]
+    dec_b = decode_bytes(w, kv_eb)
+    app_b = append_bytes(w, kv_eb)
     step_b = dec_b + app_b
     flops = attention_flops(w)
     prefill = is_prefill(w)
@@ -498,41 +525,66 @@ def main():
     # calls of several row tiles take the append and the attention as two launches
     one_tile = (w.num_q_heads // w.num_kv_heads) * w.k_draft <= (64 if w.head_dim <= 128 else 32)
     fused = bool(reps[0].t_new) and not args.separate and one_tile
+    multi_wave = not one_tile and cd in ("f16", "bf16", "fp8")  # LDS-shared row tiles
+    attn_name = "attn_append_kernel" if fused else ("tile_kernel" if multi_wave else "attn_kernel")
+
+    # Each launch of the step with its own algorithmic bytes: the shared-prefix
+    # pass reads the shared positions once and the queries of the rows it
+    # serves; the attention launch the rest of the step's bytes (with the
+    # append's when fused).  Split partials are not algorithmic: reported as
+    # overhead (written once, read once by the merge).
+    D, hkv = w.head_dim, w.num_kv_heads
+    prefix_kv_b = stats["prefix_kv_tokens"] * hkv * D * 2 * kv_eb
+    prefix_b = prefix_kv_b + stats["prefix_query_rows"] * hkv * D * e if stats["prefix_workgroups"] else 0
+    own = {3: ("prefix_kernel", prefix_b), 0: (attn_name, dec_b - prefix_kv_b + (app_b if fused else 0)),
+           2: ("append_kernel", app_b), 1: ("merge_kernel", 0)}
+    kernels, kernel_us_step, traffic = [], 0.0, 0
+    for k in (3, 2, 0, 1):
+        ms, n = kern[k]
+        if not n:
+            continue
+        name, b = own[k]
+        avg_us = 1e3 * ms / n
+        per_step = n / args.steps
+        kernel_us_step += avg_us * per_step
+        t = measured_traffic(wkey, name)
+        traffic = None if (t is None or traffic is None) else traffic + t * per_step
+        kernels.append({"kernel": name, "avg_us": round(avg_us, 2), "launches_per_step": round(per_step, 3),
+                        "bytes": b, "gbs": round(b / (avg_us * 1e-6) / 1e9, 1) if b else None,
+                        "frac_hbm": round(b / (avg_us * 1e-6) / 1e9 / PEAK_GBS, 4) if b else None,
+                        "traffic": t})
     roof = None
-    if kern[0][1]:
-        attn_ms = kern[0][0] / kern[0][1]
-        timing = "HIP events around each launch on its stream, over a second pass of the timed steps"
-        # A step that is this one launch and nothing else on the stream: the
-        # timed region's events bound its duration from above (the gaps between
-        # launches included), without the per-launch events that stretch it.
-        one_launch = kern[0][1] == args.steps and not any(kern[k][1] for k in (1, 2, 3))
-        if one_launch and ms_step < attn_ms:
-            attn_ms = ms_step
-            timing = ("HIP events on the launch stream around the timed region; each step is this one launch, "
-                      "so region / steps bounds its duration from above")
-        # a fused launch also reads the new rows and writes them into the pool
-        launch_b = dec_b + (app_b if fused else 0)
-        multi_wave = not one_tile and cd in ("f16", "bf16", "fp8")  # LDS-shared row tiles
-        kname = "attn_append_kernel" if fused else ("tile_kernel" if multi_wave else "attn_kernel")
-        achieved = launch_b / (attn_ms * 1e-3) / 1e9
+    if kernels:
+        # Summed kernel time of a step: the per-launch events (which stretch
+        # each launch a little) and the timed region / steps (which adds the
+        # gaps between launches) both bound it from above; the smaller is used.
+        step_us = kernel_us_step
+        timing = "HIP events around each launch on its stream (second pass of the timed steps), summed per step"
+        if ms_step * 1e3 < step_us:
+            step_us = ms_step * 1e3
+            timing = "HIP events on the launch stream around the timed region / steps (launch gaps included)"
+        one_launch = len(kernels) == 1 and kernels[0]["launches_per_step"] == 1
+        what = kernels[0]["kernel"] if one_launch else "step: " + " + ".join(k["kernel"] for k in kernels)
+        achieved = step_b / (step_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_GBS, 4), "traffic": measured_traffic(wkey, kname),
-                "kernel": kname, "avg_us": round(attn_ms * 1e3, 2), "bytes_per_launch": launch_b,
-                "timing": timing,
-                "avg_us_per_launch_events": round(1e3 * kern[0][0] / kern[0][1], 2)}
+                "frac": round(achieved / PEAK_GBS, 4), "traffic": None if traffic is None else int(traffic),
+                "kernel": what, "avg_us": round(step_us, 2), "bytes_per_launch": step_b, "timing": timing,
+                "kernel_us_events": round(kernel_us_step, 2)}
+        peak = PEAK_TFLOPS[w.dtype if cd != "fp8" else "bf16"]
+        tf = flops / (step_us * 1e-6) / 1e12
+        mfma = {"achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s", "frac": round(tf / peak, 4),
+                "flops_per_step": flops}
         if prefill:
-            # the shared-prefix pass does not run here; the merge launch is
-            # reported in kernel_us
-            tf = flops / (attn_ms * 1e-3) / 1e12
-            peak = PEAK_TFLOPS[w.dtype]
-            roof.update({"bound": "mfma", "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
-                         "frac": round(tf / peak, 4), "flops_per_launch": flops,
-                         "hbm_gbs": round(achieved, 1)})
+            roof.update({"bound": "mfma", "achieved": mfma["achieved"], "peak": peak, "unit": "TFLOP/s",
+                         "frac": mfma["frac"], "flops_per_launch": flops, "hbm_gbs": round(achieved, 1)})
+        elif w.k_draft > 1:
+            roof["mfma"] = mfma  # verify: G x K_d query rows per kv head, reported against both roofs
     line = {
         "metric": METRIC_PREFILL if prefill else METRIC, "value": round(value, 2),
         "unit": "TFLOP/s" if prefill else "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "us_per_step": round(ms_step * 1e3, 2),
-        "pct_of_peak": round(100 * value / (PEAK_TFLOPS[w.dtype] if prefill else PEAK_GBS), 2), "higher_is_better": True, "scaling": "weak",
+        "pct_of_peak": round(100 * value / (PEAK_TFLOPS[w.dtype] if prefill else PEAK_GBS), 2),
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"{wkey}: {describe(w)}" + (
                        "; key/value pools in E4M3 with one scale per kv head (amax / 448)" if cd == "fp8" else ""),
@@ -542,10 +594,10 @@ def main():
                    "partition_tokens_used": pt_used, "shared_prefix_workgroups": prefix_wgs,
                    "bytes_per_step": step_b, "decode_bytes": dec_b, "append_bytes": app_b,
                    "cached_tokens": int(sum(step_lengths(w))), "attention_flops": flops},
-        "kernel_us": {"attention": round(1e3 * kern[0][0] / max(1, kern[0][1]), 2),
-                      "merge": round(1e3 * kern[1][0] / max(1, kern[1][1]), 2) if kern[1][1] else None,
-                      "append": round(1e3 * kern[2][0] / max(1, kern[2][1]), 2) if kern[2][1] else None,
-                      "shared_prefix": round(1e3 * kern[3][0] / max(1, kern[3][1]), 2) if kern[3][1] else None},
+        "kernels": kernels,
+        "split_overhead": {"partial_rows": stats["partial_rows"],
+                           "partial_bytes_written": stats["partial_rows"] * (D + 2) * 4,
+                           "what": "split-KV partials, written once and read once by the merge; not algorithmic"},
         "step_us_percentiles": pct,
         "host_wall_ms_per_step": round(1e3 * wall / args.steps, 4),
         "host_enqueue_us_per_step": round(1e6 * t_enq / args.steps, 2),

@@ -339,6 +339,27 @@ int pa_get_free_list(const pa_pool* pool, int32_t* out, int cap, int* n);
  * split (and before the first call). */
 int pa_last_partition(const pa_pool* pool, int* partition_tokens, int* prefix_units);
 
+/* What the pool's last successful attention call (pa_decode, pa_verify,
+ * pa_prefill, pa_append_attend, pa_decode_noalloc) launched, for measurement:
+ * the split length as pa_last_partition, the workgroups of each launch, the
+ * key/value positions the shared-prefix pass read (per kv head, each group's
+ * shared positions once) and the query rows it served (per kv head, summed
+ * over groups), and the split partial rows written (all kv heads; each row
+ * is head_dim + 2 floats, read again by the merge).  All zero before the
+ * first call. */
+typedef struct pa_call_stats {
+  int32_t partition_tokens;
+  int32_t prefix_workgroups;     /* shared-prefix launch (0: none) */
+  int32_t attention_workgroups;  /* attention workgroups of the attention launch */
+  int32_t append_workgroups;     /* append workgroups inside that launch (fused append) */
+  int32_t merge_workgroups;      /* separate merge launch (0: none, or merged inside) */
+  int32_t reserved;
+  int64_t prefix_kv_tokens;
+  int64_t prefix_query_rows;
+  int64_t partial_rows;
+} pa_call_stats;
+int pa_last_call_stats(const pa_pool* pool, pa_call_stats* out);
+
 const char* pa_strerror(int status);
 const char* pa_last_error(void);
 

@@ -56,12 +56,24 @@ SIGNATURES = {
     "pa_get_refcount": (c_int, [c_void_p, c_int, c_intp]),
     "pa_num_free_blocks": (c_int, [c_void_p, c_intp]),
     "pa_last_partition": (c_int, [c_void_p, c_intp, c_intp]),
+    "pa_last_call_stats": (c_int, [c_void_p, c_void_p]),
     "pa_get_free_list": (c_int, [c_void_p, c_i32p, c_int, c_intp]),
     "pa_strerror": (ctypes.c_char_p, [c_int]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_profile_enable": (c_int, [c_void_p, c_int]),
     "pa_profile_read": (c_int, [c_void_p, c_int, c_dblp, c_i64p]),
 }
+
+
+
+class CallStats(ctypes.Structure):
+    """pa_call_stats (include/pa.h)."""
+    _fields_ = [("partition_tokens", ctypes.c_int32), ("prefix_workgroups", ctypes.c_int32),
+                ("attention_workgroups", ctypes.c_int32), ("append_workgroups", ctypes.c_int32),
+                ("merge_workgroups", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("prefix_kv_tokens", ctypes.c_int64), ("prefix_query_rows", ctypes.c_int64),
+                ("partial_rows", ctypes.c_int64)]
+
 
 _lib = None
 

@@ -218,6 +218,12 @@ class PagedKVCache:
         abi.check(self.lib.pa_last_partition(self.handle, ctypes.byref(pt), ctypes.byref(pu)))
         return pt.value, pu.value
 
+    def last_call_stats(self) -> dict:
+        """pa_call_stats of the last attention call, as a dict."""
+        st = abi.CallStats()
+        abi.check(self.lib.pa_last_call_stats(self.handle, ctypes.byref(st)))
+        return {name: int(getattr(st, name)) for name, _ in st._fields_ if name != "reserved"}
+
     def free_list(self):
         n = ctypes.c_int()
         abi.check(self.lib.pa_get_free_list(self.handle, None, 0, ctypes.byref(n)))

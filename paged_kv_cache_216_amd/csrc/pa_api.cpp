@@ -88,6 +88,7 @@ struct pa_pool {
   char* scratch = nullptr;  // this device's fixed scratch (pa_decode_noalloc)
   int num_cus = 256;  // compute units of the pool's device
   int last_pt = 0, last_prefix_units = 0;  // of the last attention call
+  pa_call_stats last_stats{};
   // metadata ring
   Stage stage[kStages];
   int next_stage = 0;
@@ -105,6 +106,7 @@ struct pa_pool {
   std::vector<int32_t> plan_key, key_scratch;
   int plan_units = 0, plan_merges = 0;
   int64_t plan_slots = 0;
+  int64_t plan_prefix_tokens = 0, plan_prefix_rows = 0;  // shared-prefix pass: positions read, rows served
   // reused host scratch
   pa::BlockPool::Dirty dirty;
   std::vector<int32_t> slots;
@@ -329,6 +331,8 @@ void make_plan(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, int rows, 
   for (size_t m = 0; m < p->merges.size(); ++m) merge_of[p->merges[m].q_row] = static_cast<int>(m);
   const auto& pairs = p->pre_scratch;  // (group key, batch index) sorted, prefix sequences only
   const int rpw = pa::prefix_rows_per_unit(p->dtype, p->head_dim);
+  p->plan_prefix_tokens = 0;
+  p->plan_prefix_rows = 0;
   for (size_t a = 0; a < pairs.size();) {
     size_t b = a;
     while (b < pairs.size() && pairs[b].first == pairs[a].first) ++b;
@@ -340,6 +344,8 @@ void make_plan(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, int rows, 
     const int first = pairs[a].second;
     const int q_parts = p->pre_parts[first];
     const int group_rows = static_cast<int>(b - a) * rows;
+    p->plan_prefix_tokens += static_cast<int64_t>(q_parts) * pt;
+    p->plan_prefix_rows += group_rows;
     for (int q = 0; q < q_parts; ++q)
       for (int r0 = 0; r0 < group_rows; r0 += rpw)
         p->pre_units.push_back({seq_ids[first], q, r0, member0, group_rows, q_parts * pt, 0, 0});
@@ -829,6 +835,15 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   }
   p->last_pt = slots > 0 ? pt : 0;
   p->last_prefix_units = ak.n_pre_units * p->hkv;
+  pa_call_stats& cs = p->last_stats;
+  cs.partition_tokens = p->last_pt;
+  cs.prefix_workgroups = p->last_prefix_units;
+  cs.attention_workgroups = ak.n_units * p->hkv;
+  cs.append_workgroups = fused ? ak.app_blocks : 0;
+  cs.merge_workgroups = (ak.n_merges > 0 && !ak.inline_merge) ? ak.n_merges * p->hkv * rows : 0;
+  cs.prefix_kv_tokens = ak.n_pre_units > 0 ? p->plan_prefix_tokens : 0;
+  cs.prefix_query_rows = ak.n_pre_units > 0 ? p->plan_prefix_rows : 0;
+  cs.partial_rows = p->plan_slots * rows;
   return st ? release_stage(st, stream) : PA_OK;
 }
 
@@ -1245,6 +1260,12 @@ int pa_last_partition(const pa_pool* p, int* partition_tokens, int* prefix_units
   if (!p || !partition_tokens || !prefix_units) return set_err(PA_ERR_INVALID, "NULL argument");
   *partition_tokens = p->last_pt;
   *prefix_units = p->last_prefix_units;
+  return PA_OK;
+}
+
+int pa_last_call_stats(const pa_pool* p, pa_call_stats* out) {
+  if (!p || !out) return set_err(PA_ERR_INVALID, "NULL argument");
+  *out = p->last_stats;
   return PA_OK;
 }
 
