@@ -75,7 +75,10 @@ typedef enum {
  * full precision (ranksignal.fr post 218, "Quantifier"). */
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
 
-/* Create a pool over caller-owned device memory.
+/* Create a pool over caller-owned device memory: the physical pool of
+ * fixed-size blocks that every sequence's cache is cut into, each block placed
+ * anywhere in it ("PagedAttention, décodage spéculatif, MoE et Blackwell",
+ * section 1; kenji.blog "llm-inference-optimization-kv-cache", section 4.1).
  *   num_blocks      physical blocks in k_pool / v_pool (> 0)
  *   block_size      tokens per block; must be 16
  *   num_kv_heads    key/value heads per block (> 0)
@@ -105,12 +108,19 @@ int pa_create_pool(pa_pool** out, int num_blocks, int block_size, int num_kv_hea
  * own buffers.  Caller memory is not touched.  NULL is accepted. */
 int pa_destroy_pool(pa_pool* pool);
 
-/* Start sequence seq_id (0 <= seq_id < max_seqs, not live).  With
+/* Start sequence seq_id (0 <= seq_id < max_seqs, not live), holding no
+ * block until its first append: only the blocks a sequence needs are taken
+ * (kenji.blog "llm-inference-optimization-kv-cache", section 4.2).  With
  * parent_seq >= 0 (live, != seq_id) the new sequence shares the parent's first
  * ceil(shared_tokens / 16) blocks (reference counts + 1) and starts with
  * length shared_tokens (0 <= shared_tokens <= parent length): copy-on-write
- * fork.  With parent_seq < 0, shared_tokens must be 0.  Host-side only; the
- * device table rows are written by the next device call. */
+ * fork: sequences derived from one prompt point at the same physical blocks
+ * and a block is copied only when written ("PagedAttention, décodage
+ * spéculatif, MoE et Blackwell", section 1; kenji.blog page, section 4.2).
+ * With parent_seq < 0, shared_tokens must be 0.  Host-side only; the device
+ * table rows are written by the next device call.  Errors: PA_ERR_INVALID
+ * for an id out of range or live, a parent not live or shared_tokens out of
+ * range; nothing changes. */
 int pa_alloc_blocks(pa_pool* pool, int seq_id, int parent_seq, int shared_tokens);
 
 /* Block swap to host memory.  When GPU memory runs short, a KV cache can move
@@ -179,7 +189,12 @@ int pa_prefix_entries(const pa_pool* pool, int* n);
  * PA_ERR_STATE for pools of other dtypes. */
 int pa_set_kv_scales(pa_pool* pool, const float* k_scale, const float* v_scale);
 
-/* Append n_tok[i] new K/V rows to sequence seq_ids[i], i = 0..n_seq-1.
+/* Append n_tok[i] new K/V rows to sequence seq_ids[i], i = 0..n_seq-1: the
+ * key and value of every new token are stored in the cache, so that later
+ * steps read them instead of recomputing them (kenji.blog
+ * "llm-inference-optimization-kv-cache", section 3.1 and its data-flow graph);
+ * a sequence takes a new block only when its last one is full (same page,
+ * section 4.2).
  *   seq_ids, n_tok  host int32 [n_seq]; sequences live and distinct;
  *                   n_tok[i] >= 0; length + n_tok[i] <= 16 * max_blocks_per_seq
  *   k_new, v_new    device [sum(n_tok)][num_kv_heads][head_dim] in dtype, rows
@@ -208,7 +223,12 @@ int pa_append_kv(pa_pool* pool, const int32_t* seq_ids, int n_seq, const int32_t
  *                default needs); otherwise a positive
  *                multiple of 32: contexts longer than this are cut into
  *                partitions processed in parallel and merged exactly by their
- *                log-sum-exp; a value >= the longest context disables the split
+ *                log-sum-exp; a value >= the longest context disables the
+ *                split.  Partition q covers [q * pt, (q + 1) * pt) and the last
+ *                one runs to the end of the sequence; when the call has at most
+ *                16 query rows per kv head, a context of up to 1.25 * pt tokens
+ *                stays unsplit and the last partition absorbs a remainder of
+ *                up to pt / 4 tokens (so no partition is a handful of tokens)
  *   workspace    device scratch for split partials, ws_bytes long (see
  *                pa_workspace_size); may be NULL when no sequence is split.
  *                With partition_tokens = 0 the library only splits when the
@@ -261,8 +281,10 @@ int pa_decode_noalloc(pa_pool* pool, const int32_t* seq_ids, int n_seq, int num_
 
 /* Speculative verify: the last k_draft rows of each sequence are draft tokens
  * (already appended) and draft i (0-based) attends to positions
- * [0, length - k_draft + i], its own row included (P1 section 1 and P2
- * section 5.2, speculative decoding; P4 "Spéculer").
+ * [0, length - k_draft + i], its own row included (speculative decoding:
+ * "PagedAttention, décodage spéculatif, MoE et Blackwell", section 1;
+ * kenji.blog "llm-inference-optimization-kv-cache", section 5.2; ranksignal.fr
+ * post 218, "Spéculer").
  *   q, out  device [n_seq][k_draft][num_q_heads][head_dim]
  *   lse     device float [n_seq][k_draft][num_q_heads] or NULL
  * Lengths must be >= k_draft; (num_q_heads / num_kv_heads) * k_draft is at
@@ -278,7 +300,8 @@ int pa_verify(pa_pool* pool, const int32_t* seq_ids, int n_seq, int k_draft, int
  * prompt (already appended, e.g. with pa_append_kv), and chunk token i
  * (0-based) attends to positions [0, length - n_new + i].  Long prompts are
  * split into such chunks so that their attention can run between decode steps
- * (P4 "Les noyaux d'attention", chunked prefill).  The computation is exactly
+ * (ranksignal.fr post 218, "Les noyaux d'attention", chunked prefill).  The
+ * computation is exactly
  * pa_verify with k_draft = n_new; q, out, lse, limits and errors as there.  */
 int pa_prefill(pa_pool* pool, const int32_t* seq_ids, int n_seq, int n_new, int num_q_heads,
                float scale, const void* q, void* out, float* lse, int partition_tokens,
@@ -304,8 +327,13 @@ int pa_append_attend(pa_pool* pool, const int32_t* seq_ids, int n_seq, int n_new
                      int partition_tokens, void* workspace, size_t ws_bytes, void* stream);
 
 /* Cut sequence seq_id back to new_len tokens (0 <= new_len <= length), e.g. to
- * drop rejected drafts.  Blocks past ceil(new_len / 16) lose one reference and
- * go to the back of the free list, in logical order, when unreferenced. */
+ * drop rejected drafts: after a rejection, generation resumes from the first
+ * wrong draft, so the cache keeps only the accepted prefix (kenji.blog
+ * "llm-inference-optimization-kv-cache", section 5.2; ranksignal.fr post 218,
+ * "Spéculer").  Blocks past ceil(new_len / 16) lose one reference and go to
+ * the back of the free list, in logical order, when unreferenced.  Host-side
+ * only; PA_ERR_INVALID (nothing changes) for a sequence not live or new_len
+ * out of range. */
 int pa_truncate(pa_pool* pool, int seq_id, int new_len);
 
 /* pa_truncate for n_seq sequences in one call (host int32 arrays
@@ -313,7 +341,11 @@ int pa_truncate(pa_pool* pool, int seq_id, int new_len);
  * accepted drafts.  All arguments are checked first; on error nothing changes. */
 int pa_truncate_batch(pa_pool* pool, const int32_t* seq_ids, int n_seq, const int32_t* new_lens);
 
-/* End sequence seq_id: pa_truncate to 0, then the id becomes free. */
+/* End sequence seq_id: pa_truncate to 0, then the id becomes free; its blocks
+ * go back to the pool for other sequences, which is what keeps the waste of
+ * paging to the unused slots of each sequence's last block (kenji.blog
+ * "llm-inference-optimization-kv-cache", section 4.2).  Host-side only;
+ * PA_ERR_INVALID for a sequence not live. */
 int pa_free_seq(pa_pool* pool, int seq_id);
 
 /* Enqueue the pending block-table / length updates on `stream` now. */
@@ -321,7 +353,17 @@ int pa_sync_tables(pa_pool* pool, void* stream);
 
 /* Bytes of workspace that pa_decode / pa_verify need for n_seq sequences of
  * at most max_tokens tokens each with this partition_tokens (0 = the library's
- * choice) and k_draft queries per sequence (1 for decode).  0 if nothing splits. */
+ * choice) and k_draft queries per sequence (1 for decode).  0 if nothing splits.
+ * The workspace holds the split-KV partials: each partition of a long context
+ * is attended separately, its unnormalised output and (max, sum) kept in
+ * fp32, and the partitions are merged exactly by log-sum-exp -- this
+ * library's way of running one pass over a long cache in parallel while the
+ * scores and probabilities stay on chip and the output is written once
+ * (ranksignal.fr post 218, "Les noyaux d'attention").  The figure is an upper
+ * bound: it counts ceil(max_tokens / partition_tokens) partitions per
+ * sequence, at least what any call of those sizes uses (a library-chosen
+ * partition for shared prefixes is longer, never shorter).  Host-side only;
+ * PA_ERR_INVALID for bad sizes. */
 int pa_workspace_size(const pa_pool* pool, int n_seq, int num_q_heads, int k_draft,
                       int max_tokens, int partition_tokens, size_t* bytes);
 
