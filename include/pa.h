@@ -360,10 +360,11 @@ int pa_sync_tables(pa_pool* pool, void* stream);
  * library's way of running one pass over a long cache in parallel while the
  * scores and probabilities stay on chip and the output is written once
  * (ranksignal.fr post 218, "Les noyaux d'attention").  The figure is an upper
- * bound: it counts ceil(max_tokens / partition_tokens) partitions per
- * sequence, at least what any call of those sizes uses (a library-chosen
- * partition for shared prefixes is longer, never shorter).  Host-side only;
- * PA_ERR_INVALID for bad sizes. */
+ * bound: it counts ceil(max_tokens / partition_tokens) + 1 partitions per
+ * sequence, at least what any call of those sizes uses (a shared-prefix
+ * member's own partitions start where the shared prefix ends, which can take
+ * one more; a library-chosen partition for shared prefixes is longer, never
+ * shorter).  Host-side only; PA_ERR_INVALID for bad sizes. */
 int pa_workspace_size(const pa_pool* pool, int n_seq, int num_q_heads, int k_draft,
                       int max_tokens, int partition_tokens, size_t* bytes);
 

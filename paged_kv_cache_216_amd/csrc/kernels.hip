@@ -310,7 +310,7 @@ __device__ inline void store_elem(T* p, float v) {
 // metadata); the bodies resolve the token range from it after their first
 // loads are issued, so that those loads do not wait for the length.
 struct Unit {
-  int q_row, seq, n_raw, tok_begin, slot_base, nparts, part, merge, nlaunch;
+  int q_row, seq, n_raw, tok_begin, slot_base, nparts, part, merge;
   int row0, trows;  // this wave's query rows: [row0, row0 + trows) of the call's rows
   int clip_row;     // the last row of the workgroup: no position past what it sees is read
   int pre_row0, pre_member0, pre_rows;  // shared-prefix pass only
@@ -349,7 +349,8 @@ __device__ inline f32x4 load_device4(__amdgpu_buffer_rsrc_t r, int byte_off) {
 }
 
 // Merge of a split (sequence, kv head) inside the attention launch, by the
-// wave whose partition finishes last (rows <= 16, parts <= kInlineMergeParts).
+// wave that arrives last (parts <= kInlineMergeParts; one unit takes all the
+// query rows of a (sequence, kv head)).
 // Its partial stores are complete (vmcnt 0) before it counts itself in; the
 // wave that counts the last partition reads every partition's (m, l, acc) with
 // device-scope loads and writes out and lse with the same exact formula as
@@ -366,56 +367,69 @@ __device__ inline f32x4 load_device4(__amdgpu_buffer_rsrc_t r, int byte_off) {
 // measured on MI355X, batch-256 decode 64 -> 95 us and the 70B-like decode
 // 54 -> 97 us with an acq_rel increment.
 template <typename T, int D>
-__device__ inline void merge_last(const AttnParams& p, const Unit& u, int kvh) {
+__device__ inline void merge_last(const AttnParams& p, int merge, int kvh) {
   constexpr int V = D / 64;  // 16-byte column chunks per lane
-  const int lane = threadIdx.x;
+  constexpr int C = 8;       // partitions loaded at once
+  const int lane = threadIdx.x & 63;
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores have completed
-  unsigned* ctr = p.merge_ctr + u.merge * p.hkv + kvh;
+  const MergeUnit mu = p.merges[merge];
+  unsigned* ctr = p.merge_ctr + merge * p.hkv + kvh;
   unsigned old = 0;
   if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = __builtin_amdgcn_readfirstlane(old);
-  if (old != static_cast<unsigned>(u.nlaunch - 1)) return;  // (earlier partitions: a previous launch)
-  // every partition has counted itself: reset for the next launch, then merge
+  if (old != static_cast<unsigned>(mu.arrivals - 1)) return;  // (earlier partitions: a previous launch)
+  // every arrival has counted itself: reset for the next launch, then merge
   if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int P = u.nparts;
+  const int P = mu.nparts;
   const int rows = p.rows;
-  const int base = u.slot_base + kvh * P;
+  const int base = mu.slot_base + kvh * P;
   const auto racc = page_rsrc(p.ws_acc, 0x7ffffff0);
   const int c0 = (lane & 15) * (D / 16);
   for (int r0 = 0; r0 < rows; r0 += 4) {
     const int r = r0 + (lane >> 4);
     const int rr = r < rows ? r : rows - 1;
-    float m[kInlineMergeParts], l[kInlineMergeParts];
-    f32x4 a[kInlineMergeParts][V];
-#pragma unroll
-    for (int q = 0; q < kInlineMergeParts; ++q) {
-      const int qq = q < P ? q : P - 1;
-      const size_t sl = static_cast<size_t>(base + qq) * rows + rr;
-      m[q] = load_device(p.ws_ml + 2 * sl);
-      l[q] = load_device(p.ws_ml + 2 * sl + 1);
-#pragma unroll
-      for (int v = 0; v < V; ++v) a[q][v] = load_device4(racc, static_cast<int>((sl * D + c0 + 4 * v) * 4));
-    }
-    float M = m[0];
-#pragma unroll
-    for (int q = 1; q < kInlineMergeParts; ++q) M = q < P ? fmaxf(M, m[q]) : M;
-    const float mu = (M == kNegInf) ? 0.f : M;
-    float den = 0.f;
+    // partitions C at a time, combined with a running maximum (one chunk:
+    // M = max m_q, the weights 2^(m_q - M))
+    float M = kNegInf, den = 0.f;
     f32x4 num[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) num[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q0 = 0; q0 < P; q0 += C) {
+      float m[C], l[C];
+      f32x4 a[C][V];
 #pragma unroll
-    for (int q = 0; q < kInlineMergeParts; ++q) {
-      const float w = q < P ? __builtin_amdgcn_exp2f(m[q] - mu) : 0.f;
-      den += w * l[q];
+      for (int q = 0; q < C; ++q) {
+        const int qq = min(q0 + q, P - 1);
+        const size_t sl = static_cast<size_t>(base + qq) * rows + rr;
+        m[q] = load_device(p.ws_ml + 2 * sl);
+        l[q] = load_device(p.ws_ml + 2 * sl + 1);
+#pragma unroll
+        for (int v = 0; v < V; ++v) a[q][v] = load_device4(racc, static_cast<int>((sl * D + c0 + 4 * v) * 4));
+      }
+      float Mn = M;
+#pragma unroll
+      for (int q = 0; q < C; ++q) Mn = q0 + q < P ? fmaxf(Mn, m[q]) : Mn;
+      const float mu_ = (Mn == kNegInf) ? 0.f : Mn;
+      const float so = __builtin_amdgcn_exp2f(M - mu_);  // 0 on the first chunk
+      den *= so;
 #pragma unroll
       for (int v = 0; v < V; ++v)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) num[v][e] += w * a[q][v][e];
+        for (int e = 0; e < 4; ++e) num[v][e] *= so;
+#pragma unroll
+      for (int q = 0; q < C; ++q) {
+        const float w = q0 + q < P ? __builtin_amdgcn_exp2f(m[q] - mu_) : 0.f;
+        den += w * l[q];
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) num[v][e] += w * a[q][v][e];
+      }
+      M = Mn;
     }
     if (r < rows) {
       const int i = r / p.group, g = r - (r / p.group) * p.group;
-      const size_t orow = static_cast<size_t>(u.q_row * p.k_draft + i) * p.hq + kvh * p.group + g;
+      const size_t orow = static_cast<size_t>(mu.q_row * p.k_draft + i) * p.hq + kvh * p.group + g;
       const float inv = 1.f / den;
       T* op = static_cast<T*>(p.out) + orow * D + c0;
 #pragma unroll
@@ -470,7 +484,8 @@ __device__ inline uint32_t page_load4(__amdgpu_buffer_rsrc_t r, int byte_off) {
 // per thread, into one of two LDS buffers while the waves compute on the
 // other.  All W waves run the same pair loop (the unit's range is the
 // workgroup's), so the barriers line up.
-template <typename T, int D, int NT, bool NTL, bool FUSED, bool PREFIX = false, bool Q8 = false, int W = 1>
+template <typename T, int D, int NT, bool NTL, bool FUSED, bool PREFIX = false, bool Q8 = false, int W = 1,
+          bool ONE_PAIR = false>
 __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) {
   static_assert(W == 1 || !FUSED, "LDS-shared pairs: no fused append");
   using Op = typename MfmaOp<T>::type;
@@ -853,7 +868,7 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
           run(r, base_pos + 2 * pj * kBlk);
         }
       }
-    } else if constexpr (NT >= 2 && D * NT < 512 && !PREFIX) {
+    } else if constexpr (NT >= 2 && D * NT < 512 && !PREFIX && !ONE_PAIR) {
       Frag fa, fb;
       load(fa, 0);
       for (int pj = 0; pj < npairs; pj += 2) {
@@ -985,7 +1000,9 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
 
   // ---- epilogue
   if constexpr (PREFIX) {
-    // each row's partial goes to partition u.part of its own sequence
+    // each row's partial goes to partition u.part of its own sequence (at
+    // device scope when the members' merge runs in this launch)
+    const bool dev = p.pre_in_launch != 0;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const float l = wave_sum_groups(l_run[nt]);
@@ -998,7 +1015,13 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
           const int slot = m.slot_base + kvh * m.nparts + u.part;
           float* ap = p.ws_acc + (static_cast<size_t>(slot) * rows + (r - j * rows)) * D;
 #pragma unroll
-          for (int c = 0; c < DC; ++c) ap[16 * c + col] = acc[nt][c][jj] * vsc;  // (E4M3: the head's V scale)
+          for (int c = 0; c < DC; ++c) {
+            const float x = acc[nt][c][jj] * vsc;  // (E4M3: the head's V scale)
+            if (dev)
+              store_device(ap + 16 * c + col, x);
+            else
+              ap[16 * c + col] = x;
+          }
         }
       }
       const int r = u.pre_row0 + nt * 16 + col;
@@ -1007,8 +1030,22 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
         const PrefixMember m = p.pre_members[u.pre_member0 + j];
         const int slot = m.slot_base + kvh * m.nparts + u.part;
         float* mp = p.ws_ml + (static_cast<size_t>(slot) * rows + (r - j * rows)) * 2;
-        mp[0] = m_run[nt];
-        mp[1] = l;
+        if (dev) {
+          store_device(mp, m_run[nt]);
+          store_device(mp + 1, l);
+        } else {
+          mp[0] = m_run[nt];
+          mp[1] = l;
+        }
+      }
+    }
+    if constexpr (W == 1) {
+      if (dev) {
+        // every member whose rows this wave holds: count this arrival, and
+        // the last arrival merges the member
+        const int r_end = min(u.pre_row0 + 16 * NT, u.pre_rows);
+        for (int j = u.pre_row0 / rows; j * rows < r_end; ++j)
+          merge_last<T, D>(p, p.pre_members[u.pre_member0 + j].merge, kvh);
       }
     }
     return;
@@ -1051,7 +1088,7 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
           float* ap = p.ws_acc + (static_cast<size_t>(slot) * rows + u.row0 + r) * D;
 #pragma unroll
           for (int c = 0; c < DC; ++c) {
-            if constexpr (NT == 1)
+            if (p.inline_merge)
               store_device(ap + 16 * c + col, acc[nt][c][jj] * vsc);
             else
               ap[16 * c + col] = acc[nt][c][jj] * vsc;
@@ -1061,7 +1098,7 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       const int r = nt * 16 + col;
       if (grp == 0 && r < u.trows) {
         float* mp = p.ws_ml + (static_cast<size_t>(slot) * rows + u.row0 + r) * 2;
-        if constexpr (NT == 1) {
+        if (p.inline_merge) {
           store_device(mp, m_run[nt]);
           store_device(mp + 1, l);
         } else {
@@ -1071,8 +1108,8 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       }
     }
   }
-  if constexpr (NT == 1) {
-    if (p.inline_merge && u.slot_base >= 0) merge_last<T, D>(p, u, kvh);
+  if constexpr (W == 1) {
+    if (p.inline_merge && u.slot_base >= 0) merge_last<T, D>(p, u.merge, kvh);
   }
 }
 
@@ -1238,7 +1275,7 @@ __device__ inline void attn_body32(const AttnParams& p, const Unit& u, int kvh) 
 }
 
 // One workgroup (one wave) per (work unit, key/value head).
-template <typename T, int D, int NT, bool NTL, bool FUSED, bool Q8 = false>
+template <typename T, int D, int NT, bool NTL, bool FUSED, bool Q8 = false, bool ONE_PAIR = false>
 __device__ inline void attn_unit(const AttnParams& p, const int32_t* meta) {
   const int unit = blockIdx.x / p.hkv;
   const int kvh = blockIdx.x - unit * p.hkv;
@@ -1250,7 +1287,6 @@ __device__ inline void attn_unit(const AttnParams& p, const int32_t* meta) {
   u.nparts = w.nparts;
   u.part = w.part;
   u.merge = w.merge;
-  u.nlaunch = w.nlaunch;
   // The length travels as a vector load (then made uniform), so that the
   // bodies' first loads are issued while it is on its way instead of after it.
   if constexpr (FUSED) {
@@ -1259,14 +1295,14 @@ __device__ inline void attn_unit(const AttnParams& p, const int32_t* meta) {
     const auto lens = page_rsrc(p.seq_len, 0x7ffffff0);
     u.n_raw = __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(lens, w.seq * 4, 0, 0));
   }
-  u.tok_begin = w.nparts > 1 ? w.part * p.part_tokens : 0;
+  u.tok_begin = w.tok_begin;
   u.row0 = w.row0;
   u.trows = min(p.tile_rows, p.rows - w.row0);
   u.clip_row = u.row0 + u.trows - 1;
   if constexpr (std::is_same_v<T, float>)
     attn_body32<D, NT>(p, u, kvh);
   else
-    attn_body16<T, D, NT, NTL, FUSED, false, Q8>(p, u, kvh);
+    attn_body16<T, D, NT, NTL, FUSED, false, Q8, 1, ONE_PAIR>(p, u, kvh);
 }
 
 template <typename T, int D, int NT, bool NTL, bool Q8 = false>
@@ -1299,10 +1335,9 @@ void tile_kernel(AttnParams p) {
   u.nparts = w.nparts;
   u.part = w.part;
   u.merge = w.merge;
-  u.nlaunch = w.nlaunch;
   const auto lens = page_rsrc(p.seq_len, 0x7ffffff0);
   u.n_raw = __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(lens, w.seq * 4, 0, 0));
-  u.tok_begin = w.nparts > 1 ? w.part * p.part_tokens : 0;
+  u.tok_begin = w.tok_begin;
   const int g_rows = min(p.tile_rows, p.rows - w.row0);
   u.row0 = w.row0 + wave * 16 * NT;
   // a wave past the tile's rows (trows <= 0) still loads its share of every
@@ -1345,13 +1380,13 @@ struct PrefixShape {
   static constexpr int kWavesPerSimd = D <= 128 ? 2 : 1;  // resident waves per SIMD
 };
 
-template <typename T, int D, bool Q8 = false>
-__global__ __launch_bounds__((64 * PrefixShape<D, Q8>::W)) __attribute__((amdgpu_waves_per_eu((PrefixShape<D, Q8>::kWavesPerSimd))))
-void prefix_kernel(AttnParams p) {
+// Unit `unit` of the shared-prefix pass (workgroup `unit * hkv + kvh`).
+template <typename T, int D, bool Q8>
+__device__ inline void prefix_unit(const AttnParams& p, int block) {
   using Shape = PrefixShape<D, Q8>;
   constexpr int NT = Shape::NT;
-  const int unit = blockIdx.x / p.hkv;
-  const int kvh = blockIdx.x - unit * p.hkv;
+  const int unit = block / p.hkv;
+  const int kvh = block - unit * p.hkv;
   const PrefixUnit pu = p.pre_units[unit];
   // With several waves per workgroup, a wave past the group's rows still
   // loads its share of every pair and meets every barrier; its queries repeat
@@ -1361,7 +1396,7 @@ void prefix_kernel(AttnParams p) {
   if (Shape::W == 1 && row0 >= pu.group_rows) return;
   Unit u{};
   u.seq = pu.seq;
-  u.n_raw = pu.prefix_tokens;
+  u.n_raw = pu.prefix_tokens;  // the last partition of the prefix ends at the shared positions
   u.part = pu.part;
   u.tok_begin = pu.part * p.part_tokens;
   u.nparts = 1 << 30;  // a partition never the last: tokens [tok_begin, min(prefix, tok_begin + part_tokens))
@@ -1374,6 +1409,36 @@ void prefix_kernel(AttnParams p) {
   u.clip_row = 1 << 24;
   // the prefix blocks are read by every row block of the group: cached loads
   attn_body16<T, D, NT, false, false, true, Q8, Shape::W>(p, u, kvh);
+}
+
+template <typename T, int D, bool Q8 = false>
+__global__ __launch_bounds__((64 * PrefixShape<D, Q8>::W)) __attribute__((amdgpu_waves_per_eu((PrefixShape<D, Q8>::kWavesPerSimd))))
+void prefix_kernel(AttnParams p) {
+  prefix_unit<T, D, Q8>(p, blockIdx.x);
+}
+
+// Attention units, then the shared-prefix units, then (FUSED) the append work,
+// in one launch of single-wave workgroups (16-bit pools): the pass over the
+// shared prefix overlaps the members' own partitions, and the last wave to
+// finish partials of a (member, kv head) merges them.  Multi-tile units keep
+// one pair in flight here, so that the launch holds two waves per SIMD as the
+// prefix pass needs.
+template <typename T, int D, int NT, bool FUSED>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
+void attn_prefix_kernel(AttnParams p, InlineMeta im) {
+  const int32_t* meta = p.app.ext ? p.app.ext : im.w;
+  const int n_attn = p.n_units * p.hkv;
+  const int n_pre = p.n_pre_units * p.hkv;
+  const int b = blockIdx.x;
+  if (b < n_attn) {
+    attn_unit<T, D, NT, false, FUSED, false, true>(p, meta);
+    return;
+  }
+  if (b < n_attn + n_pre) {
+    prefix_unit<T, D, false>(p, b - n_attn);
+    return;
+  }
+  if constexpr (FUSED) append_work<static_cast<int>(sizeof(T))>(p.app, meta, b - n_attn - n_pre, 64);
 }
 
 // Exact merge of one output row of a split sequence, one 256-thread workgroup
@@ -1456,6 +1521,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
 
 template <typename T, int D, int NT, bool NTL, bool Q8>
 void launch_attn_nt(const AttnParams& p, const InlineMeta& m, hipStream_t stream) {
+  if constexpr (!std::is_same_v<T, float> && !Q8 && !NTL && (D <= 128 ? NT <= 2 : NT == 1)) {
+    if (p.pre_in_launch) {
+      const dim3 grid(static_cast<unsigned>(p.n_units + p.n_pre_units) * p.hkv + (p.t_new > 0 ? p.app_blocks : 0));
+      if (p.t_new > 0)
+        hipLaunchKernelGGL((attn_prefix_kernel<T, D, NT, true>), grid, dim3(64), 0, stream, p, m);
+      else
+        hipLaunchKernelGGL((attn_prefix_kernel<T, D, NT, false>), grid, dim3(64), 0, stream, p, m);
+      return;
+    }
+  }
   if constexpr (!std::is_same_v<T, float>) {
     if (p.t_new > 0) {
       const dim3 grid(static_cast<unsigned>(p.n_units) * p.hkv + p.app_blocks);
@@ -1538,6 +1613,11 @@ int prefix_units_t(int head_dim) {
   }
 }
 }  // namespace
+
+// (wider row tiles would not fit the two waves per SIMD the pass needs)
+bool prefix_in_attention_launch(int dtype, int head_dim, int rows) {
+  return (dtype == kBF16 || dtype == kF16) && rows <= (head_dim <= 128 ? 32 : 16);
+}
 
 int prefix_rows_per_unit(int dtype, int head_dim) {
   return dtype == kFP8 ? prefix_rows_t<true>(head_dim) : prefix_rows_t<false>(head_dim);
@@ -1628,7 +1708,8 @@ hipError_t launch_merge(DType dt, const AttnParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_attention(DType dt, const AttnParams& p, const InlineMeta* meta, hipStream_t stream) {
-  if (p.n_units == 0 && (p.t_new == 0 || p.app_blocks == 0)) return hipSuccess;
+  if (p.n_units == 0 && (p.t_new == 0 || p.app_blocks == 0) && !(p.pre_in_launch && p.n_pre_units > 0))
+    return hipSuccess;
   switch (dt) {
     case kBF16: return launch_attn_t<__bf16>(p, *meta, stream);
     case kFP8: return launch_attn_t<__bf16, true>(p, *meta, stream);

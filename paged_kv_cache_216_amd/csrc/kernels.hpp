@@ -45,7 +45,8 @@ struct AppendParams {
 // key/value head comes from the grid.  Lengths are not part of the unit: the
 // kernel reads them from the device length mirror (or, when the launch also
 // appends, from the call's metadata), so a plan stays valid while sequences
-// grow inside their partitions.
+// grow inside their partitions.  A partition covers [tok_begin, tok_begin +
+// part_tokens); the last one runs to the end of the sequence.
 struct WorkUnit {
   int32_t q_row;      // index of the sequence in q / out (0..n_seq-1)
   int32_t seq;        // row of the block table and of the length mirror
@@ -55,8 +56,7 @@ struct WorkUnit {
   int32_t row0;       // first query row of the unit's tile: calls with more rows
                       // than one unit takes (tile_rows) have one unit per tile
   int32_t merge;      // split sequences: index of its MergeUnit; else -1
-  int32_t nlaunch;    // partitions of this sequence computed by this launch (the
-                      // others, if any, by the shared-prefix pass before it)
+  int32_t tok_begin;  // first position of the partition
 };
 
 // Shared-prefix pass.  Sequences of a batch that are copy-on-write forks of
@@ -70,7 +70,7 @@ struct PrefixMember {
   int32_t q_row;      // index of the sequence in q / out
   int32_t slot_base;  // its partial slot of kv head 0, part 0
   int32_t nparts;     // its partitions
-  int32_t pad;
+  int32_t merge;      // its MergeUnit
 };
 
 struct PrefixUnit {
@@ -79,16 +79,20 @@ struct PrefixUnit {
   int32_t row0;           // first row of the group's rows (member * rows + row) for this wave
   int32_t member0;        // the group's first entry in the member array
   int32_t group_rows;     // members * rows
-  int32_t prefix_tokens;
+  int32_t prefix_tokens;  // the shared positions; the last partition ends there
   int32_t pad0, pad1;
 };
 
-// One split sequence: its partials are merged into out / lse.
+// One split sequence: its partials are merged into out / lse.  With the
+// in-launch merge, `arrivals` is the number of times per kv head that a wave
+// of the merging launch finishes partials of this sequence (its own
+// partitions, and the shared-prefix waves covering its rows when they run in
+// the same launch); the wave that arrives last merges.
 struct MergeUnit {
   int32_t q_row;
   int32_t slot_base;
   int32_t nparts;
-  int32_t pad;
+  int32_t arrivals;
 };
 
 struct AttnParams {
@@ -122,10 +126,11 @@ struct AttnParams {
   int lens_by_row;
   int app_blocks;
   AppendParams app;
-  // In-launch merge (inline_merge = 1): the last partition of a split
-  // (sequence, kv head) to finish merges all of them; merge_ctr[merge * hkv +
-  // kvh] counts finished partitions and is zero between launches.  Used when
-  // every split sequence has at most kInlineMergeParts partitions and rows <= 16.
+  // In-launch merge (inline_merge = 1): the last wave to finish partials of a
+  // split (sequence, kv head) merges all of them; merge_ctr[merge * hkv + kvh]
+  // counts the arrivals and is zero between launches.  Used when every split
+  // sequence has at most kInlineMergeParts partitions and one unit takes all
+  // query rows of a (sequence, kv head).
   unsigned* merge_ctr;
   int inline_merge;
   const float* kv_scale;  // E4M3 pools: [4][hkv] k_scale, v_scale, 1/k_scale, 1/v_scale
@@ -133,17 +138,25 @@ struct AttnParams {
   const PrefixUnit* pre_units;
   const PrefixMember* pre_members;
   int n_pre_units;
+  // 1: the shared-prefix units run in the attention launch itself, after the
+  // attention units (16-bit pools, in-launch merge)
+  int pre_in_launch;
 };
 
-constexpr int kInlineMergeParts = 8;
+constexpr int kInlineMergeParts = 16;
 
 hipError_t launch_append(const AppendParams& p, const InlineMeta* meta, hipStream_t stream);
 hipError_t launch_attention(DType dt, const AttnParams& p, const InlineMeta* meta, hipStream_t stream);
 hipError_t launch_merge(DType dt, const AttnParams& p, hipStream_t stream);
-// The shared-prefix pass (16-bit dtypes); run before launch_attention.
+// The shared-prefix pass as a launch of its own, run before launch_attention
+// (when pre_in_launch is 0).
 hipError_t launch_prefix(DType dt, const AttnParams& p, hipStream_t stream);
 // Query rows one workgroup of the shared-prefix pass takes, for a head dim.
 int prefix_rows_per_unit(int dtype, int head_dim);
+// Whether the shared-prefix pass can run inside the attention launch of a
+// call with `rows` query rows per kv head (its workgroups are single waves,
+// as the attention's are, and both fit the same registers).
+bool prefix_in_attention_launch(int dtype, int head_dim, int rows);
 // workgroups of the shared-prefix pass one compute unit holds at once
 int prefix_units_per_cu(int dtype, int head_dim);
 // Workgroups of 64 threads that the append work of `p` needs.

@@ -117,12 +117,14 @@ struct pa_pool {
   std::vector<pa::MergeUnit> merges;
   std::vector<int> lens, parts;
   // shared-prefix pass: partitions of each sequence done by the pass (0 = none)
-  std::vector<int> pre_parts;
+  // and the shared positions they cover (the sequence's own partitions start there)
+  std::vector<int> pre_parts, pre_shared;
   std::vector<std::pair<int32_t, int>> pre_scratch;
   std::vector<PrefixGroup> pre_groups;
   std::vector<pa::PrefixUnit> pre_units;
   std::vector<pa::PrefixMember> pre_members;
   int plan_pre_units = 0;
+  bool plan_pre_in_launch = false;
   std::vector<int32_t> ntok;
   // call metadata being assembled, and its kernel-argument copy
   std::vector<int32_t> meta;
@@ -262,16 +264,22 @@ int rows_limit(const pa_pool* p) { return pa::max_rows_for_head_dim(p->head_dim)
 // pt / 4 tokens, so no partition is a handful of tokens whose merge lands at
 // the end of the launch (measured on MI355X: 70B-like decode 53.9 -> 53.4 us;
 // for verify's 20-row units the longer last partitions cost 4 %).
+int parts_of(int n, int pt, int rows) {
+  const int slack = rows <= 16 ? pt / 4 : 0;
+  return (pt > 0 && n > pt + slack) ? (n - slack + pt - 1) / pt : 1;
+}
+
+int64_t count_slots(const pa_pool* p, int n_seq) {
+  int64_t slots = 0;
+  for (int i = 0; i < n_seq; ++i)
+    if (p->parts[i] > 1) slots += static_cast<int64_t>(p->parts[i]) * p->hkv;
+  return slots;
+}
+
 int64_t count_parts(pa_pool* p, int n_seq, int pt, int rows) {
   p->parts.resize(n_seq);
-  int64_t slots = 0;
-  const int slack = rows <= 16 ? pt / 4 : 0;
-  for (int i = 0; i < n_seq; ++i) {
-    const int n = p->lens[i];
-    p->parts[i] = (pt > 0 && n > pt + slack) ? (n - slack + pt - 1) / pt : 1;
-    if (p->parts[i] > 1) slots += static_cast<int64_t>(p->parts[i]) * p->hkv;
-  }
-  return slots;
+  for (int i = 0; i < n_seq; ++i) p->parts[i] = parts_of(p->lens[i], pt, rows);
+  return count_slots(p, n_seq);
 }
 
 // Work decomposition: one unit per (sequence, partition, tile of query rows);
@@ -279,7 +287,14 @@ int64_t count_parts(pa_pool* p, int n_seq, int pt, int rows) {
 // a sequence), shared by the sequence's row tiles.  Units that read a whole
 // partition first, then the rest by the tokens they read (causal limit
 // included), most first, so the grid's tail holds the short ones.
-void make_plan(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, int rows, int group, int k_draft) {
+// A split sequence that belongs to a shared-prefix group has partitions
+// [0, q) from the shared-prefix pass ([j pt, min((j + 1) pt, shared))) and its
+// own partitions from `shared` on.  With the in-launch merge, each merge unit
+// counts the arrivals that the merging launch makes for it: its own units, and
+// when the pass runs in the same launch (pre_in_launch), one per pass wave
+// whose rows include the sequence's.
+void make_plan(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, int rows, int group, int k_draft,
+               bool pre_in_launch) {
   std::vector<pa::WorkUnit>& units = p->units;
   auto& tail = p->tail_units;
   units.clear();
@@ -293,25 +308,29 @@ void make_plan(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, int rows, 
     const int base = parts == 1 ? -1 : static_cast<int>(slots);
     const int merge = parts == 1 ? -1 : static_cast<int>(p->merges.size());
     const int q0 = p->pre_parts[i];  // partitions done by the shared-prefix pass
+    const int own0 = q0 > 0 ? p->pre_shared[i] : 0;  // first position of the sequence's own partitions
     if (parts > 1) slots += static_cast<int64_t>(parts) * p->hkv;
+    int own_units = 0;
     for (int row0 = 0; row0 < rows; row0 += tr) {
       const int last_row = std::min(rows, row0 + tr) - 1;
       const int visible = n - k_draft + last_row / group + 1;  // tokens the tile's last row sees
       if (parts == 1) {
-        tail.push_back({std::min(n, visible), {i, seq_ids[i], 0, 1, -1, row0, -1, 1}});
+        tail.push_back({std::min(n, visible), {i, seq_ids[i], 0, 1, -1, row0, -1, 0}});
         continue;
       }
       for (int q = q0; q < parts; ++q) {
-        const int end = q == parts - 1 ? n : (q + 1) * pt;  // the last partition runs to the end
-        const int len = std::max(0, std::min(end, visible) - q * pt);
-        const pa::WorkUnit u{i, seq_ids[i], q, parts, base, row0, merge, parts - q0};
+        const int begin = own0 + (q - q0) * pt;
+        const int end = q == parts - 1 ? n : begin + pt;  // the last partition runs to the end
+        const int len = std::max(0, std::min(end, visible) - begin);
+        const pa::WorkUnit u{i, seq_ids[i], q, parts, base, row0, merge, begin};
+        ++own_units;
         if (len == pt)
           units.push_back(u);
         else
           tail.push_back({len, u});
       }
     }
-    if (parts > 1) p->merges.push_back({i, base, parts, 0});
+    if (parts > 1) p->merges.push_back({i, base, parts, own_units});
   }
   std::sort(tail.begin(), tail.end(), [](const auto& a, const auto& b) {
     if (a.first != b.first) return a.first > b.first;
@@ -338,17 +357,25 @@ void make_plan(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, int rows, 
     while (b < pairs.size() && pairs[b].first == pairs[a].first) ++b;
     const int member0 = static_cast<int>(p->pre_members.size());
     for (size_t k = a; k < b; ++k) {
-      const pa::MergeUnit& mu = p->merges[merge_of[pairs[k].second]];
-      p->pre_members.push_back({pairs[k].second, mu.slot_base, mu.nparts, 0});
+      const int m = merge_of[pairs[k].second];
+      const pa::MergeUnit& mu = p->merges[m];
+      p->pre_members.push_back({pairs[k].second, mu.slot_base, mu.nparts, m});
     }
     const int first = pairs[a].second;
     const int q_parts = p->pre_parts[first];
+    const int shared = p->pre_shared[first];
     const int group_rows = static_cast<int>(b - a) * rows;
-    p->plan_prefix_tokens += static_cast<int64_t>(q_parts) * pt;
+    p->plan_prefix_tokens += shared;
     p->plan_prefix_rows += group_rows;
     for (int q = 0; q < q_parts; ++q)
-      for (int r0 = 0; r0 < group_rows; r0 += rpw)
-        p->pre_units.push_back({seq_ids[first], q, r0, member0, group_rows, q_parts * pt, 0, 0});
+      for (int r0 = 0; r0 < group_rows; r0 += rpw) {
+        p->pre_units.push_back({seq_ids[first], q, r0, member0, group_rows, shared, 0, 0});
+        if (pre_in_launch) {
+          // this wave arrives once for every member whose rows it holds
+          const int r_end = std::min(r0 + rpw, group_rows);
+          for (int j = r0 / rows; j * rows < r_end; ++j) p->merges[merge_of[pairs[a + j].second]].arrivals += 1;
+        }
+      }
     a = b;
   }
 }
@@ -360,8 +387,9 @@ void make_plan(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, int rows, 
 // batch index), sorted by group.
 constexpr int kPrefixMinGroup = 4;
 
-void find_prefix_groups(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, int k_draft) {
+void find_prefix_groups(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, int k_draft, int rows) {
   p->pre_parts.assign(n_seq, 0);
+  p->pre_shared.assign(n_seq, 0);
   p->pre_groups.clear();
   auto& pairs = p->pre_scratch;
   pairs.clear();
@@ -388,14 +416,17 @@ void find_prefix_groups(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, i
         blocks = j;
       }
       const int shared = std::min(blocks * pa::kBlock, limit);
-      // whole partitions only, never a member's last one (it runs to the
-      // member's end, past the shared blocks)
-      int q_parts = shared / pt;
-      for (size_t k = a; k < b; ++k) q_parts = std::min(q_parts, p->parts[pairs[k].second] - 1);
-      if (q_parts > 0) {
+      // the pass takes the whole shared prefix, its last partition ending at
+      // `shared` (at least one whole partition); each member's own partitions
+      // start there, and it keeps at least one (its drafts lie past `shared`)
+      if (shared >= pt) {
+        const int q_parts = (shared + pt - 1) / pt;
         p->pre_groups.push_back({shared, static_cast<int>(b - a)});
         for (size_t k = a; k < b; ++k) {
-          p->pre_parts[pairs[k].second] = q_parts;
+          const int i = pairs[k].second;
+          p->pre_parts[i] = q_parts;
+          p->pre_shared[i] = shared;
+          p->parts[i] = q_parts + parts_of(p->lens[i] - shared, pt, rows);
           pairs[out++] = pairs[k];
         }
       }
@@ -413,24 +444,32 @@ void find_prefix_groups(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, i
 // (generations x tokens per wave) is taken, the shortest on ties.  (Measured
 // on MI355X, 64 forks of a 4,096-token prefix with 5 drafts: 512-token
 // partitions give 2,560 waves for 2,048 slots and a 105 us step; 608 gives
-// 1,920 waves and 88 us.)
-int prefix_partition(const pa_pool* p, int pt0, int rows) {
+// 1,920 waves and 88 us.)  When the pass shares the attention launch, that
+// launch's own waves (one per sequence and kv head at least) count too:
+// measured for the same workload in one launch, 512 -> 111, 768 -> 87,
+// 896 -> 82, 1,024 -> 83, 1,344 -> 91 us.
+int prefix_partition(const pa_pool* p, int pt0, int rows, int64_t other_waves) {
   if (p->pre_groups.empty()) return pt0;
   const int64_t rpw = pa::prefix_rows_per_unit(p->dtype, p->head_dim);
   const int64_t resident = static_cast<int64_t>(p->num_cus) * pa::prefix_units_per_cu(p->dtype, p->head_dim);
-  auto waves = [&](int pt) {  // workgroups of the pass
-    int64_t w = 0;
+  auto waves = [&](int pt) {  // workgroups of the pass (groups with a whole partition), and the launch's others
+    int64_t w = other_waves;
     for (const PrefixGroup& g : p->pre_groups)
-      w += static_cast<int64_t>(g.shared / pt) * ((static_cast<int64_t>(g.members) * rows + rpw - 1) / rpw) * p->hkv;
+      if (g.shared >= pt)
+        w += static_cast<int64_t>((g.shared + pt - 1) / pt) *
+             ((static_cast<int64_t>(g.members) * rows + rpw - 1) / rpw) * p->hkv;
     return w;
   };
   const int64_t w0 = waves(pt0);
   if (w0 <= resident) return pt0;
+  // the shortest partition whose waves fit one generation, else the one with
+  // the fewest generations x tokens per wave
   int best = pt0;
   int64_t best_cost = (w0 + resident - 1) / resident * pt0;
   for (int pt = pt0 + 32; pt <= 2 * pt0; pt += 32) {
     const int64_t w = waves(pt);
-    if (w == 0) break;  // no whole partition left in any prefix
+    if (w == other_waves) break;  // no whole partition left in any prefix
+    if (w <= resident) return pt;
     const int64_t cost = (w + resident - 1) / resident * pt;
     if (cost < best_cost) {
       best = pt;
@@ -669,28 +708,53 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   }
 
   // forks sharing a prefix: its partitions are computed once for all of them
-  find_prefix_groups(p, seq_ids, n_seq, pt, k_draft);
+  find_prefix_groups(p, seq_ids, n_seq, pt, k_draft, rows);
   if (partition_tokens == 0 && pt > 0) {
-    // a longer partition never needs more workspace than the one checked above
-    const int best = prefix_partition(p, pt, rows);
+    // the launch's other waves, when the pass runs inside the attention launch
+    const int64_t others = (pa::prefix_in_attention_launch(p->dtype, p->head_dim, rows) && rows <= rows_limit(p))
+                               ? static_cast<int64_t>(n_seq) * p->hkv
+                               : 0;
+    const int best = prefix_partition(p, pt, rows, others);
     if (best != pt) {
       pt = best;
-      slots = count_parts(p, n_seq, pt, rows);
-      find_prefix_groups(p, seq_ids, n_seq, pt, k_draft);
+      count_parts(p, n_seq, pt, rows);
+      find_prefix_groups(p, seq_ids, n_seq, pt, k_draft, rows);
     }
   }
+  slots = count_slots(p, n_seq);
+  if (slots && plan_ws_bytes(p, slots, rows) > ws_bytes) {
+    // a member's own partitions start at the end of the shared prefix, which
+    // can take one partition more than the plain split checked above: without
+    // the room for it, no shared-prefix pass (the plain split fits: a longer
+    // library-chosen partition needs no more than the default)
+    p->pre_parts.assign(n_seq, 0);
+    p->pre_shared.assign(n_seq, 0);
+    p->pre_scratch.clear();
+    p->pre_groups.clear();
+    slots = count_parts(p, n_seq, pt, rows);
+  }
+  // Merges inside the attention launch (the last wave to finish a split
+  // (sequence, kv head)'s partials merges them) when one unit takes all query
+  // rows of a (sequence, kv head) and no sequence has too many partitions; the
+  // shared-prefix units then run in that launch too (16-bit pools).
+  int max_parts = 0;
+  for (int i = 0; i < n_seq; ++i) max_parts = std::max(max_parts, p->parts[i]);
+  const bool inline_merge = p->dtype != PA_F32 && rows <= rows_limit(p) && max_parts <= pa::kInlineMergeParts &&
+                            ws_bytes < (size_t{1} << 31);
+  const bool pre_in_launch = inline_merge && !p->pre_groups.empty() && pa::prefix_in_attention_launch(p->dtype, p->head_dim, rows);
 
   // reuse the device plan when the batch, its partition structure and the
   // shared-prefix grouping are unchanged
   std::vector<int32_t>& key = p->key_scratch;
-  key.assign({pt, n_seq, rows});
+  key.assign({pt, n_seq, rows, inline_merge ? 1 : 0, pre_in_launch ? 1 : 0});
   for (int i = 0; i < n_seq; ++i) {
     key.push_back(seq_ids[i]);
     key.push_back(p->parts[i]);
     key.push_back(p->pre_parts[i]);
+    key.push_back(p->pre_shared[i]);
   }
   if (key != p->plan_key) {
-    make_plan(p, seq_ids, n_seq, pt, rows, group, k_draft);
+    make_plan(p, seq_ids, n_seq, pt, rows, group, k_draft, pre_in_launch);
     p->plan_key.swap(key);
     p->plan_units = static_cast<int>(p->units.size());
     p->plan_merges = static_cast<int>(p->merges.size());
@@ -784,14 +848,14 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   ak.tile_rows = pa::tile_rows_for_call(p->dtype, p->head_dim, rows);
   ak.head_dim = p->head_dim;
   ak.scale_log2 = scale * 1.4426950408889634f;
-  ak.stream_kv = p->bp.num_shared() == 0 ? 1 : 0;
+  ak.stream_kv = (p->bp.num_shared() == 0 && !pre_in_launch) ? 1 : 0;
   ak.app = base_append(p);
   // Short splits (few partitions, one row tile) are merged inside the
   // attention launch by the last partition to finish; others by merge_kernel.
   ak.merge_ctr = merge_ctr;
   ak.kv_scale = p->kv_scale;
-  ak.inline_merge = (p->dtype != PA_F32 && rows <= 16 && p->plan_max_parts <= pa::kInlineMergeParts &&
-                     ws_bytes < (size_t{1} << 31)) ? 1 : 0;
+  ak.inline_merge = inline_merge ? 1 : 0;
+  ak.pre_in_launch = pre_in_launch ? 1 : 0;
   Stage* st = nullptr;
   if (fused) {
     // metadata: this append's table / length updates, the new rows' slots, and
@@ -812,14 +876,14 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
     if (rc != PA_OK) return rc;
   }
   const pa::DType dt = static_cast<pa::DType>(p->dtype);
-  if (ak.n_pre_units > 0) {
+  if (ak.n_pre_units > 0 && !pre_in_launch) {
     ProfEvent ev{};
     if (!noalloc) prof_begin(p, 3, stream, &ev);
     hipError_t e = pa::launch_prefix(dt, ak, stream);
     if (e != hipSuccess) return hip_err(e, "shared-prefix kernel");
     if (!noalloc) prof_end(p, stream, &ev);
   }
-  if (ak.n_units > 0 || fused) {
+  if (ak.n_units > 0 || fused || (pre_in_launch && ak.n_pre_units > 0)) {
     ProfEvent ev{};
     if (!noalloc) prof_begin(p, 0, stream, &ev);
     hipError_t e = pa::launch_attention(dt, ak, &p->inline_meta, stream);
@@ -1225,7 +1289,9 @@ int pa_workspace_size(const pa_pool* p, int n_seq, int num_q_heads, int k_draft,
     return set_err(PA_ERR_INVALID, "partition_tokens must be 0 or a positive multiple of 32");
   const int64_t rows = static_cast<int64_t>(num_q_heads / p->hkv) * k_draft;
   const int pt = partition_tokens == 0 ? default_partition(rows) : partition_tokens;
-  const int64_t parts = max_tokens > pt ? (max_tokens + pt - 1) / pt : 0;
+  // (one partition more than the plain split: a shared-prefix member's own
+  // partitions start where its shared prefix ends)
+  const int64_t parts = max_tokens > pt ? (max_tokens + pt - 1) / pt + 1 : 0;
   *bytes = static_cast<size_t>(n_seq) * parts * p->hkv * rows * (p->head_dim + 2) * sizeof(float);
   return PA_OK;
 }

@@ -143,6 +143,12 @@ class Pair:
         assert self.gpu.free_list() == list(self.model.free)
 
 
+def prefix_pass_ran(gpu) -> bool:
+    """Whether the last attention call ran the shared-prefix pass (as a launch
+    of its own or inside the attention launch)."""
+    return gpu.last_call_stats()["prefix_workgroups"] > 0
+
+
 def oracle_decode(pair: Pair, seqs, q_bits: np.ndarray, scale: float, k_draft: int = 1):
     """Oracle O [n, K, Hq, D] and lse [n, K, Hq] read through the model's pool."""
     m = pair.model

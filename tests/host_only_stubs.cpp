@@ -25,6 +25,7 @@ hipError_t launch_merge(DType, const AttnParams&, hipStream_t) { unreachable("la
 hipError_t launch_prefix(DType, const AttnParams&, hipStream_t) { unreachable("launch_prefix"); }
 int prefix_rows_per_unit(int, int) { unreachable("prefix_rows_per_unit"); }
 int prefix_units_per_cu(int, int) { unreachable("prefix_units_per_cu"); }
+bool prefix_in_attention_launch(int, int, int) { unreachable("prefix_in_attention_launch"); }
 int append_blocks64(const AppendParams&) { unreachable("append_blocks64"); }
 int max_rows_for_head_dim(int) { unreachable("max_rows_for_head_dim"); }
 int tile_rows_for_call(int, int, int) { unreachable("tile_rows_for_call"); }

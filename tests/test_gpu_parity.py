@@ -8,7 +8,7 @@ import pytest
 import torch
 
 from gpu_harness import (FILL, Pair, assert_close, contiguous_reference, oracle_decode, pool_bits,
-                         to_torch)
+                         prefix_pass_ran, to_torch)
 from paged_kv_cache_216_amd import PaInvalid, PaNoMem
 from workloads import make_custom, make_gqa70b, make_highbatch, make_long, make_tiny, make_verify
 from workloads.synth import _to_storage as to_storage
@@ -368,13 +368,15 @@ def _check_verify_partition(pair):
     # prefix pass would need 8 partitions x 40 row blocks x 8 kv heads = 2,560
     # workgroups, more than one round of the 8 per CU the device holds at
     # once; the chosen length (a multiple of 32, at most twice the default)
-    # fits the pass into one round.
+    # fits the pass into one round.  The pass takes the whole 4,096-token
+    # prefix (its last partition ends at 4,096).
     pt, prefix_wgs = pair.gpu.last_partition()
     resident = 8 * torch.cuda.get_device_properties(0).multi_processor_count
     assert pt % 32 == 0 and 512 <= pt <= 1024, pt
-    assert prefix_wgs == (4096 // pt) * 40 * 8, (pt, prefix_wgs)
+    assert prefix_wgs == -(-4096 // pt) * 40 * 8, (pt, prefix_wgs)
     if 8 * 40 * 8 > resident:
         assert prefix_wgs <= resident, (pt, prefix_wgs, resident)
+    assert pair.gpu.last_call_stats()["prefix_kv_tokens"] == 4096
 
 
 def test_full_verify():
@@ -444,12 +446,9 @@ def test_shared_prefix_pass(prefix_len, k_draft, dtype):
     shared.fill()
     shared.append_step_rows()
     seqs = list(range(w.batch))
-    shared.gpu.profile_enable(True)
     a, la = _decode(shared, seqs, w.q, w.scale, pt=512, k_draft=k_draft)
     torch.cuda.synchronize()
-    _, n_prefix = shared.gpu.profile_read(3)
-    shared.gpu.profile_enable(False)
-    assert n_prefix == 1, "the shared-prefix launch did not run"
+    assert prefix_pass_ran(shared.gpu), "the shared-prefix pass did not run"
     ro, rl = oracle_decode(shared, seqs, w.q, w.scale, k_draft=k_draft)
     assert_close(a, la, ro, rl, dtype, "shared-prefix pass")
     nb = (len(seqs) + 1) * w.num_blocks
@@ -459,11 +458,9 @@ def test_shared_prefix_pass(prefix_len, k_draft, dtype):
         k = np.concatenate([w.prefix_k, w.k_rows[s], w.new_k[s]])
         v = np.concatenate([w.prefix_v, w.v_rows[s], w.new_v[s]])
         private.append([s], [k.shape[0]], k, v)
-    private.gpu.profile_enable(True)
     b, lb = _decode(private, seqs, w.q, w.scale, pt=512, k_draft=k_draft)
     torch.cuda.synchronize()
-    assert private.gpu.profile_read(3)[1] == 0
-    private.gpu.profile_enable(False)
+    assert not prefix_pass_ran(private.gpu)
     assert_close(b, lb, ro, rl, dtype, "private copies")
 
 
@@ -485,25 +482,25 @@ def test_last_partition_absorbs_remainder_boundaries(pt, lengths):
     assert_close(out, lse, ro, rl, "bf16", f"absorbed remainders pt={pt}")
 
 
-def test_shared_prefix_forks_with_unsplit_members():
+def test_shared_prefix_forks_with_short_members():
     """Decode over six forks of a 530-token prefix at 512-token partitions:
-    members up to 640 tokens run unsplit (their last partition absorbs the
-    remainder), so no whole partition is split in every member and the
-    shared-prefix launch must not run; outputs match the oracle."""
+    the members' first appends copied the partly filled 34th block, so they
+    share 528 positions; the pass takes them whole (a 512-token partition and
+    a 16-token one) and each member keeps its own rest, unsplit as a short
+    sequence would be.  Outputs match the oracle, and the structure is what the
+    library reports."""
     w = make_custom(lengths=[10, 60, 100, 30, 200, 5], mode="append_decode", num_q_heads=16, num_kv_heads=4,
                     head_dim=128, dtype="bf16", seed=41, prefix_len=530)
     pair = Pair(w)
     pair.fill()
     pair.append_step_rows()
     seqs = list(range(w.batch))
-    pair.gpu.profile_enable(True)
     out, lse = _decode(pair, seqs, w.q, w.scale, pt=512)
     torch.cuda.synchronize()
-    _, n_prefix = pair.gpu.profile_read(3)
-    pair.gpu.profile_enable(False)
-    assert n_prefix == 0, "a shared-prefix launch ran over unsplit members"
+    st = pair.gpu.last_call_stats()
+    assert st["prefix_kv_tokens"] == 528 and st["prefix_workgroups"] > 0, st
     ro, rl = oracle_decode(pair, seqs, w.q, w.scale)
-    assert_close(out, lse, ro, rl, "bf16", "forks with unsplit members")
+    assert_close(out, lse, ro, rl, "bf16", "forks with short members")
 
 
 def test_shared_prefix_pass_fused_append_decode():

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_harness import Pair, assert_close, oracle_decode, to_torch
+from gpu_harness import Pair, assert_close, oracle_decode, to_torch, prefix_pass_ran
 from workloads import make_custom
 
 pytestmark = pytest.mark.gpu
@@ -181,11 +181,8 @@ def test_prefill_shared_prefix_forks():
     pair.fill()
     pair.append_step_rows()
     seqs = list(range(w.batch))
-    pair.gpu.profile_enable(True)
     out, lse = _prefill(pair, seqs, 512)
     torch.cuda.synchronize()
-    n_prefix = pair.gpu.profile_read(3)[1]
-    pair.gpu.profile_enable(False)
-    assert n_prefix == 1
+    assert prefix_pass_ran(pair.gpu)
     ro, rl = oracle_decode(pair, seqs, w.q, w.scale, k_draft=24)
     assert_close(out, lse, ro, rl, "bf16", "prefill over a shared prefix")

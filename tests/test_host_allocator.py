@@ -78,6 +78,7 @@ def test_host_only_pool_refuses_attention():
 
 def test_workspace_size_formula():
     lib = PagedKVCache(8, 8, 128, "f16", 8, 2048, host_only=True)
-    # 8 sequences of 32768 tokens, 512-token partitions, 32 query heads: 8*64*8 slots x 4 rows x (128+2) floats
-    assert lib.workspace_size(8, 32, 32768, 1, 512) == 8 * 64 * 8 * 4 * 130 * 4
+    # 8 sequences of 32768 tokens, 512-token partitions (64, plus one for a shared
+    # prefix's end), 32 query heads: 8*65*8 slots x 4 rows x (128+2) floats
+    assert lib.workspace_size(8, 32, 32768, 1, 512) == 8 * 65 * 8 * 4 * 130 * 4
     assert lib.workspace_size(8, 32, 512, 1, 512) == 0
