@@ -326,6 +326,42 @@ int pa_append_attend(pa_pool* pool, const int32_t* seq_ids, int n_seq, int n_new
                      const void* v_new, int num_q_heads, float scale, const void* q, void* out, float* lse,
                      int partition_tokens, void* workspace, size_t ws_bytes, void* stream);
 
+/* Graph steps.  Serving engines record a step's kernel launches once and
+ * replay the recording every step instead of launching kernel by kernel,
+ * padding each batch to a few fixed size classes and updating the data the
+ * recording points at in place between replays ("CUDA Graphs, modèles de
+ * raisonnement et service désagrégé", section 1).  A graph step is the step
+ * of pa_append_attend (append n_new rows to each sequence, then attend) split
+ * in two:
+ *
+ * pa_graph_prepare: the step's host bookkeeping and everything that cannot be
+ *   replayed, eagerly on `stream` -- pending table changes, and the whole
+ *   append when it needs copy-on-write copies -- then one copy, on `stream`,
+ *   of the step's metadata (lengths, slots of the new rows, table updates) and
+ *   work plan into a buffer that the library keeps for the step's class.  The
+ *   class is the number of work units rounded up to a power of two (at least
+ *   16), with n_new: *class_units (may be NULL) returns it.  Arguments as
+ *   pa_append_attend, with these limits: 16-bit or E4M3 pools; (num_q_heads /
+ *   num_kv_heads) * n_new within one unit's rows (64, 32 at head_dim 256); the
+ *   partition is partition_tokens or the library's default, every step, and the
+ *   workspace must hold the step's partials (PA_ERR_INVALID otherwise); at most
+ *   16 partitions per sequence (PA_ERR_STATE otherwise); no shared-prefix pass.
+ *   Results are bitwise those of pa_append_attend with the same partition
+ *   (the appended rows too).  On error nothing changes.
+ * pa_graph_launch: enqueue the attention + append launch of the last prepared
+ *   step on `stream`: one kernel, whose grid is padded to the class (its
+ *   workgroups past the step's units and rows have nothing to do) and whose
+ *   arguments point only at the class's buffer, the pool and the caller's
+ *   buffers.  It can be captured into a HIP graph; a replay after a later
+ *   pa_graph_prepare of the same class runs that step.  Replays use the
+ *   buffers (q, out, lse, k_new, v_new, workspace) and the scale given to the
+ *   prepare before the capture: pass the same ones to every prepare of a
+ *   class.  PA_ERR_STATE before any prepare. */
+int pa_graph_prepare(pa_pool* pool, const int32_t* seq_ids, int n_seq, int n_new, const void* k_new,
+                     const void* v_new, int num_q_heads, float scale, const void* q, void* out, float* lse,
+                     int partition_tokens, void* workspace, size_t ws_bytes, void* stream, int* class_units);
+int pa_graph_launch(pa_pool* pool, void* stream);
+
 /* Cut sequence seq_id back to new_len tokens (0 <= new_len <= length), e.g. to
  * drop rejected drafts: after a rejection, generation resumes from the first
  * wrong draft, so the cache keeps only the accepted prefix (kenji.blog

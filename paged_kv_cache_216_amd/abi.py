@@ -47,6 +47,9 @@ SIGNATURES = {
                            c_int, c_void_p, c_size_t, c_void_p]),
     "pa_append_attend": (c_int, [c_void_p, c_i32p, c_int, c_int, c_void_p, c_void_p, c_int, c_float, c_void_p,
                                  c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
+    "pa_graph_prepare": (c_int, [c_void_p, c_i32p, c_int, c_int, c_void_p, c_void_p, c_int, c_float, c_void_p,
+                                 c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_void_p, c_intp]),
+    "pa_graph_launch": (c_int, [c_void_p, c_void_p]),
     "pa_truncate": (c_int, [c_void_p, c_int, c_int]),
     "pa_truncate_batch": (c_int, [c_void_p, c_i32p, c_int, c_i32p]),
     "pa_free_seq": (c_int, [c_void_p, c_int]),

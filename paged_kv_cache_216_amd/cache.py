@@ -326,6 +326,30 @@ class PagedKVCache:
                                             ws_bytes, _stream(stream)))
         return out, lse
 
+    def graph_prepare(self, seq_ids, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, scale: float,
+                      out: torch.Tensor, lse: Optional[torch.Tensor], partition_tokens: int = 0,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> int:
+        """pa_graph_prepare: the host part of a graph step (append n_new rows per
+        sequence, then attend); returns the step's class (padded units)."""
+        n_seq, n_new, hq, d = q.shape
+        self._check_rows(k_new, n_seq * n_new)
+        self._check_rows(v_new, n_seq * n_new)
+        if q.dtype != self.tdtype or not q.is_contiguous() or d != self.d or out.shape != q.shape:
+            raise ValueError("q and out must be contiguous [n_seq, n_new, Hq, D] tensors in the pool dtype")
+        ids, n = abi.i32_array(seq_ids)
+        if n != n_seq:
+            raise ValueError("one query set per sequence")
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        cls = ctypes.c_int()
+        abi.check(self.lib.pa_graph_prepare(self.handle, ids, n, n_new, _ptr(k_new), _ptr(v_new), hq, float(scale),
+                                            _ptr(q), _ptr(out), _ptr(lse), partition_tokens, _ptr(workspace),
+                                            ws_bytes, _stream(stream), ctypes.byref(cls)))
+        return cls.value
+
+    def graph_launch(self, stream=None) -> None:
+        """pa_graph_launch: enqueue (or, under capture, record) the last prepared step."""
+        abi.check(self.lib.pa_graph_launch(self.handle, _stream(stream)))
+
     def _attend(self, seq_ids, kd, q, hq, scale, out, lse, want_lse, pt, ws, stream):
         if q.dtype != self.tdtype or not q.is_contiguous() or q.shape[-1] != self.d:
             raise ValueError("q must be contiguous, in the pool dtype, with the pool head_dim")

@@ -1356,9 +1356,26 @@ template <typename T, int D, int NT, bool NTL, bool Q8 = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 && D == 128 ? 2 : 1)))
 void attn_append_kernel(AttnParams p, InlineMeta im) {
   const int32_t* meta = p.app.ext ? p.app.ext : im.w;
+  const int b = blockIdx.x;
+  if (p.graph_units > 0) {
+    // a graph step: this step's counts from its metadata; workgroups of the
+    // padded grid past them have nothing to do
+    const int n_grid = p.graph_units * p.hkv;
+    if (b >= n_grid) {
+      AppendParams a = p.app;
+      a.n_tab = meta[kGraphTab];
+      a.n_len = meta[kGraphLen];
+      a.n_rows = meta[kGraphRows];
+      append_work<Q8 ? 1 : static_cast<int>(sizeof(T))>(a, meta, b - n_grid, 64);
+      return;
+    }
+    if (b >= meta[kGraphUnits] * p.hkv) return;
+    attn_unit<T, D, NT, NTL, true, Q8>(p, meta);
+    return;
+  }
   const int n_attn = p.n_units * p.hkv;
-  if (static_cast<int>(blockIdx.x) >= n_attn) {
-    append_work<Q8 ? 1 : static_cast<int>(sizeof(T))>(p.app, meta, blockIdx.x - n_attn, 64);
+  if (b >= n_attn) {
+    append_work<Q8 ? 1 : static_cast<int>(sizeof(T))>(p.app, meta, b - n_attn, 64);
     return;
   }
   attn_unit<T, D, NT, NTL, true, Q8>(p, meta);

@@ -141,7 +141,16 @@ struct AttnParams {
   // 1: the shared-prefix units run in the attention launch itself, after the
   // attention units (16-bit pools, in-launch merge)
   int pre_in_launch;
+  // Graph steps (graph_units > 0, fused append + attention): the grid is
+  // padded to graph_units units and the launch's append workgroups, and the
+  // counts that change from step to step are read from the head of the step's
+  // metadata (kGraph* words below) instead of from these parameters.
+  int graph_units;
 };
+
+// Head of a graph step's metadata: the units of this step, and the table
+// updates, length updates and new rows of its append.
+constexpr int kGraphUnits = 0, kGraphTab = 1, kGraphLen = 2, kGraphRows = 3, kGraphHeader = 8;
 
 constexpr int kInlineMergeParts = 16;
 

@@ -16,6 +16,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <map>
 #include <cstring>
 #include <new>
 #include <string>
@@ -71,6 +72,19 @@ struct ProfEvent {
 // how many sequences of the call it has.
 struct PrefixGroup {
   int shared, members;
+};
+
+// Graph steps of one capacity class (units of the padded grid, rows appended
+// per sequence): a device buffer holding the step's metadata and its plan,
+// the in-launch merge counters, and the launch parameters, which point at
+// them and so stay the same from step to step.
+struct GraphClass {
+  void* buf = nullptr;
+  unsigned* ctr = nullptr;
+  pa::AttnParams params{};
+  int units = 0, n_new = 0;
+  size_t tab_cap = 0, words = 0;
+  size_t off_lens = 0, off_slots = 0, off_tab = 0, off_len = 0, off_units = 0, off_merges = 0;
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -129,6 +143,10 @@ struct pa_pool {
   // call metadata being assembled, and its kernel-argument copy
   std::vector<int32_t> meta;
   pa::InlineMeta inline_meta;
+  // graph steps: classes by (units, rows appended per sequence), and the one
+  // the last pa_graph_prepare filled
+  std::map<std::pair<int, int>, GraphClass> gclass;
+  GraphClass* glast = nullptr;
   // profiling
   bool prof = false;
   std::vector<ProfEvent> prof_events;
@@ -911,6 +929,213 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   return st ? release_stage(st, stream) : PA_OK;
 }
 
+// The classes graph steps are padded to: units rounded up to a power of two,
+// at least 16.
+int graph_class_units(int units) {
+  int c = 16;
+  while (c < units) c *= 2;
+  return c;
+}
+
+int ensure_graph_class(pa_pool* p, int units, int n_new, GraphClass** out) {
+  GraphClass& g = p->gclass[{units, n_new}];
+  if (!g.buf) {
+    g.units = units;
+    g.n_new = n_new;
+    const size_t c = static_cast<size_t>(units);
+    // table entries a sequence's append can open: one per 16 rows, plus one
+    g.tab_cap = c * (static_cast<size_t>(n_new) / pa::kBlock + 2);
+    auto up8 = [](size_t x) { return (x + 7) / 8 * 8; };
+    g.off_lens = pa::kGraphHeader;
+    g.off_slots = up8(g.off_lens + c);
+    g.off_tab = up8(g.off_slots + c * n_new);
+    g.off_len = up8(g.off_tab + 2 * g.tab_cap);
+    g.off_units = up8(g.off_len + 2 * c);
+    g.off_merges = g.off_units + 8 * c;
+    g.words = g.off_merges + 4 * c;
+    hipError_t e = hipMalloc(&g.buf, g.words * sizeof(int32_t));
+    if (e == hipSuccess) e = hipMalloc(&g.ctr, c * p->hkv * sizeof(unsigned));
+    if (e == hipSuccess) e = hipMemset(g.ctr, 0, c * p->hkv * sizeof(unsigned));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      if (g.buf) (void)hipFree(g.buf);
+      if (g.ctr) (void)hipFree(g.ctr);
+      p->gclass.erase({units, n_new});
+      return hip_err(e, "graph step buffers");
+    }
+  }
+  *out = &g;
+  return PA_OK;
+}
+
+// Host side of a graph step (pa_graph_prepare): the append's bookkeeping and
+// any work that cannot be replayed (pending table changes, copy-on-write
+// copies) run eagerly on the stream; the step's metadata and plan go into its
+// class's buffer by one copy on the stream; the launch parameters, which only
+// point at that buffer, are kept for pa_graph_launch.
+int graph_prepare(pa_pool* p, const int32_t* seq_ids, int n_seq, int n_new, const void* k_new, const void* v_new,
+                  int num_q_heads, float scale, const void* q, void* out, float* lse, int partition_tokens,
+                  void* workspace, size_t ws_bytes, void* stream_v, int* class_units) {
+  if (!p) return set_err(PA_ERR_INVALID, "pool is NULL");
+  if (p->host_only) return set_err(PA_ERR_STATE, "host-only pool has no device memory");
+  if (p->dtype == PA_F32) return set_err(PA_ERR_STATE, "graph steps take 16-bit or E4M3 pools");
+  if (n_seq < 1 || n_new < 1) return set_err(PA_ERR_INVALID, "n_seq and n_new must be >= 1");
+  if (!seq_ids || !q || !out || !k_new || !v_new) return set_err(PA_ERR_INVALID, "NULL argument");
+  if (num_q_heads <= 0 || num_q_heads % p->hkv != 0)
+    return set_err(PA_ERR_INVALID, "num_q_heads must be a positive multiple of num_kv_heads");
+  const int group = num_q_heads / p->hkv;
+  const int64_t rows64 = static_cast<int64_t>(group) * n_new;
+  if (rows64 > rows_limit(p))
+    return set_err(PA_ERR_STATE, "graph steps take calls whose query rows per kv head fit one unit");
+  const int rows = static_cast<int>(rows64);
+  if (partition_tokens < 0 || (partition_tokens > 0 && partition_tokens % 32 != 0))
+    return set_err(PA_ERR_INVALID, "partition_tokens must be 0 or a positive multiple of 32");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace) || !aligned16(k_new) || !aligned16(v_new))
+    return set_err(PA_ERR_INVALID, "q, out, workspace, k_new and v_new must be 16-byte aligned");
+  if (ws_bytes >= (size_t{1} << 31)) return set_err(PA_ERR_INVALID, "workspace of 2 GiB or more");
+  p->lens.resize(n_seq);
+  for (int i = 0; i < n_seq; ++i) {
+    if (!p->bp.live(seq_ids[i])) return set_err(PA_ERR_INVALID, "attention over a sequence that is not live");
+    p->lens[i] = p->bp.length(seq_ids[i]) + n_new;
+  }
+  // the same partition length every step: the library's default (or the
+  // caller's), and the workspace must hold its partials
+  const int pt = partition_tokens ? partition_tokens : default_partition(rows);
+  const int64_t slots = count_parts(p, n_seq, pt, rows);
+  if (slots && (!workspace || plan_ws_bytes(p, slots, rows) > ws_bytes))
+    return set_err(PA_ERR_INVALID, "graph steps need a workspace that holds this step's split partials");
+  int max_parts = 0;
+  for (int i = 0; i < n_seq; ++i) max_parts = std::max(max_parts, p->parts[i]);
+  if (max_parts > pa::kInlineMergeParts)
+    return set_err(PA_ERR_STATE, "graph steps merge inside the launch: a sequence has too many partitions");
+  p->pre_parts.assign(n_seq, 0);  // no shared-prefix pass in graph steps
+  p->pre_shared.assign(n_seq, 0);
+  p->pre_scratch.clear();
+  p->pre_groups.clear();
+  hipStream_t stream = static_cast<hipStream_t>(stream_v);
+
+  // changes made since the last call reach the device first, eagerly
+  int rc = flush_dirty(p, stream);
+  if (rc != PA_OK) return rc;
+  p->ntok.assign(n_seq, n_new);
+  p->slots.clear();
+  p->cows.clear();
+  std::string err;
+  rc = p->bp.append(seq_ids, n_seq, p->ntok.data(), &p->slots, &p->cows, &err);
+  if (rc != pa::kOk) return set_err(rc, err);
+  // an append with copies runs eagerly, whole; the replay's append part then
+  // has nothing to do (its attention still takes the new rows from k_new / v_new)
+  const bool eager_append = !p->cows.empty();
+  p->bp.take_dirty(&p->dirty);
+  if (eager_append) {
+    rc = launch_append_call(p, k_new, v_new, stream);
+    if (rc != PA_OK) return rc;
+  }
+  make_plan(p, seq_ids, n_seq, pt, rows, group, n_new, false);
+  p->plan_key.clear();  // the pool's own plan cache no longer matches its host plan
+  const int units = static_cast<int>(p->units.size());
+  GraphClass* g = nullptr;
+  rc = ensure_graph_class(p, graph_class_units(units), n_new, &g);
+  if (rc != PA_OK) return rc;
+  const pa::BlockPool::Dirty& d = p->dirty;
+  const size_t n_tab = eager_append ? 0 : d.table_idx.size();
+  const size_t n_len = eager_append ? 0 : d.len_seq.size();
+  const size_t n_rows = eager_append ? 0 : p->slots.size();
+  if (n_tab > g->tab_cap) return set_err(PA_ERR_STATE, "graph step: more table updates than its class holds");
+
+  // the step's metadata and plan, in the class's layout
+  std::vector<int32_t>& w = p->meta;
+  w.assign(g->words, 0);
+  w[pa::kGraphUnits] = units;
+  w[pa::kGraphTab] = static_cast<int32_t>(n_tab);
+  w[pa::kGraphLen] = static_cast<int32_t>(n_len);
+  w[pa::kGraphRows] = static_cast<int32_t>(n_rows);
+  for (int i = 0; i < n_seq; ++i) w[g->off_lens + i] = p->lens[i];
+  for (size_t r = 0; r < n_rows; ++r) w[g->off_slots + r] = p->slots[r];
+  for (size_t i = 0; i < n_tab; ++i) {
+    w[g->off_tab + 2 * i] = d.table_idx[i];
+    w[g->off_tab + 2 * i + 1] = d.table_val[i];
+  }
+  for (size_t i = 0; i < n_len; ++i) {
+    w[g->off_len + 2 * i] = d.len_seq[i];
+    w[g->off_len + 2 * i + 1] = d.len_val[i];
+  }
+  std::memcpy(w.data() + g->off_units, p->units.data(), 8 * p->units.size() * sizeof(int32_t));
+  std::memcpy(w.data() + g->off_merges, p->merges.data(), 4 * p->merges.size() * sizeof(int32_t));
+  Stage* st = nullptr;
+  rc = acquire_stage(p, w.size(), &st);
+  if (rc != PA_OK) return rc;
+  std::memcpy(st->host, w.data(), w.size() * sizeof(int32_t));
+  hipError_t e = hipMemcpyAsync(g->buf, st->host, w.size() * sizeof(int32_t), hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync(graph step)");
+  rc = release_stage(st, stream);
+  if (rc != PA_OK) return rc;
+
+  // launch parameters: the padded grid, pointers into the class's buffer
+  const int32_t* buf = static_cast<const int32_t*>(g->buf);
+  pa::AttnParams& ak = g->params;
+  ak = pa::AttnParams{};
+  ak.k_pool = p->k_pool;
+  ak.v_pool = p->v_pool;
+  ak.block_table = p->block_table;
+  ak.seq_len = p->seq_len;
+  ak.max_blocks = p->bp.max_blocks_per_seq();
+  ak.num_blocks = p->num_blocks;
+  ak.part_tokens = pt;
+  ak.q = q;
+  ak.out = out;
+  ak.lse = lse;
+  float* ws = static_cast<float*>(workspace);
+  ak.ws_acc = ws;
+  // the (m, l) pairs after every partial row the workspace can hold
+  const int64_t ws_slots = ws ? static_cast<int64_t>(ws_bytes / (sizeof(float) * (p->head_dim + 2) * rows)) : 0;
+  ak.ws_ml = ws ? ws + static_cast<size_t>(ws_slots) * rows * p->head_dim : nullptr;
+  ak.units = reinterpret_cast<const pa::WorkUnit*>(buf + g->off_units);
+  ak.merges = reinterpret_cast<const pa::MergeUnit*>(buf + g->off_merges);
+  ak.n_units = g->units;
+  ak.hkv = p->hkv;
+  ak.hq = num_q_heads;
+  ak.group = group;
+  ak.k_draft = n_new;
+  ak.rows = rows;
+  ak.tile_rows = pa::tile_rows_for_call(p->dtype, p->head_dim, rows);
+  ak.head_dim = p->head_dim;
+  ak.scale_log2 = scale * 1.4426950408889634f;
+  ak.stream_kv = 1;  // (a hint only: shared blocks are read correctly either way)
+  ak.t_new = n_new;
+  ak.lens_by_row = static_cast<int>(g->off_lens);
+  ak.merge_ctr = g->ctr;
+  ak.inline_merge = 1;
+  ak.kv_scale = p->kv_scale;
+  ak.graph_units = g->units;
+  ak.app = base_append(p);
+  ak.app.ext = buf;
+  ak.app.tab = static_cast<int>(g->off_tab);
+  ak.app.lens = static_cast<int>(g->off_len);
+  ak.app.slots = static_cast<int>(g->off_slots);
+  ak.app.k_new = k_new;
+  ak.app.v_new = v_new;
+  // the grid's append part: what the class's largest append needs
+  {
+    pa::AppendParams cap = ak.app;
+    cap.n_tab = static_cast<int>(g->tab_cap);
+    cap.n_len = g->units;
+    cap.n_rows = g->units * n_new;
+    ak.app_blocks = pa::append_blocks64(cap);
+  }
+  p->glast = g;
+  p->last_pt = slots > 0 ? pt : 0;
+  p->last_prefix_units = 0;
+  pa_call_stats& cs = p->last_stats;
+  cs = pa_call_stats{};
+  cs.partition_tokens = p->last_pt;
+  cs.attention_workgroups = units * p->hkv;
+  cs.append_workgroups = ak.app_blocks;
+  cs.partial_rows = slots * rows;
+  if (class_units) *class_units = g->units;
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1009,7 +1234,11 @@ int pa_destroy_pool(pa_pool* p) {
     (void)hipEventDestroy(ev.start);
     (void)hipEventDestroy(ev.stop);
   }
-  if (p->dplan || p->merge_ctr || p->kv_scale) (void)hipDeviceSynchronize();
+  if (p->dplan || p->merge_ctr || p->kv_scale || !p->gclass.empty()) (void)hipDeviceSynchronize();
+  for (auto& kv : p->gclass) {
+    if (kv.second.buf) (void)hipFree(kv.second.buf);
+    if (kv.second.ctr) (void)hipFree(kv.second.ctr);
+  }
   if (p->dplan) (void)hipFree(p->dplan);
   if (p->merge_ctr) (void)hipFree(p->merge_ctr);
   if (p->kv_scale) (void)hipFree(p->kv_scale);
@@ -1242,6 +1471,22 @@ int pa_append_attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int n_new, c
   const AppendSpec app{n_new, k_new, v_new};
   return attend(p, seq_ids, n_seq, n_new, num_q_heads, scale, q, out, lse, partition_tokens, workspace,
                 ws_bytes, stream, &app);
+}
+
+int pa_graph_prepare(pa_pool* p, const int32_t* seq_ids, int n_seq, int n_new, const void* k_new, const void* v_new,
+                     int num_q_heads, float scale, const void* q, void* out, float* lse, int partition_tokens,
+                     void* workspace, size_t ws_bytes, void* stream, int* class_units) {
+  return graph_prepare(p, seq_ids, n_seq, n_new, k_new, v_new, num_q_heads, scale, q, out, lse, partition_tokens,
+                       workspace, ws_bytes, stream, class_units);
+}
+
+int pa_graph_launch(pa_pool* p, void* stream) {
+  if (!p) return set_err(PA_ERR_INVALID, "pool is NULL");
+  if (!p->glast) return set_err(PA_ERR_STATE, "no graph step prepared");
+  const pa::DType dt = static_cast<pa::DType>(p->dtype);
+  hipError_t e = pa::launch_attention(dt, p->glast->params, &p->inline_meta, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_err(e, "attention kernel (graph step)");
+  return PA_OK;
 }
 
 int pa_truncate(pa_pool* p, int seq_id, int new_len) {
