@@ -11,7 +11,9 @@ workload.  Steps rotate over several pool replicas so that the working set
 Prints one JSON line.  `value` is effective GB/s of the whole step (algorithmic
 bytes of append + decode / step time); `roofline` reports the attention kernel
 alone, timed with HIP events recorded on the launch stream; `cpu_baseline` times
-the float64 CPU oracle on a bounded sample of the same workload.
+the float64 CPU oracle on a bounded sample of the same workload; `graph_step`
+(workloads whose step appends) times the same step replayed from captured
+graphs (pa_graph_prepare, then the replay), device us/step and host enqueue.
 """
 from __future__ import annotations
 
@@ -57,6 +59,8 @@ def parse():
     ap.add_argument("--separate", action="store_true",
                     help="issue the append and the attention as two calls instead of pa_append_attend")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replayed pass of the step (append workloads)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB before the timed region, so that "
                          "memory counters can be scaled against a copy of known size")
@@ -219,6 +223,68 @@ class Replica:
         abi.check(rc)
         if self.t_new:
             abi.check(lib.pa_truncate_batch(h, self.ids, w.batch, self.rollback))
+
+
+    def graph_prepare(self, stream_handle, pt):
+        """pa_graph_prepare of this replica's step; returns its class."""
+        from paged_kv_cache_216_amd import abi
+        c, w, lib = self.cache, self.w, self.cache.lib
+        vp = ctypes.c_void_p
+        ws = None if self.ws is None else vp(self.ws.data_ptr())
+        cls = ctypes.c_int()
+        abi.check(lib.pa_graph_prepare(c.handle, self.ids, w.batch, self.t_new, vp(self.k_new.data_ptr()),
+                                       vp(self.v_new.data_ptr()), w.num_q_heads, w.scale, vp(self.q.data_ptr()),
+                                       vp(self.out.data_ptr()), vp(self.lse.data_ptr()), pt, ws, self.ws_bytes,
+                                       stream_handle, ctypes.byref(cls)))
+        return cls.value
+
+    def roll_back(self):
+        from paged_kv_cache_216_amd import abi
+        abi.check(self.cache.lib.pa_truncate_batch(self.cache.handle, self.ids, self.w.batch, self.rollback))
+
+
+def graph_steps(reps, stream, steps, warmup, pt):
+    """The step as a graph replay: pa_graph_prepare (host bookkeeping; the
+    step's metadata and plan copied to the device on the stream), replay of the
+    launch captured once per (replica, class) from pa_graph_launch, then the
+    host rollback.  Returns device us/step and host enqueue us/step."""
+    import torch
+    from paged_kv_cache_216_amd import abi
+
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    cap = torch.cuda.Stream()
+    graphs = {}
+
+    def one(i):
+        j = i % len(reps)
+        r = reps[j]
+        cls = r.graph_prepare(sh, pt)
+        g = graphs.get((j, cls))
+        if g is None:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                abi.check(r.cache.lib.pa_graph_launch(r.cache.handle, ctypes.c_void_p(cap.cuda_stream)))
+            graphs[(j, cls)] = g
+        g.replay()
+        r.roll_back()
+
+    for i in range(max(warmup, len(reps))):
+        one(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        one(i)
+    t_enq = time.perf_counter() - t0
+    stop.record(stream)
+    torch.cuda.synchronize()
+    stats = reps[0].cache.last_call_stats()
+    return {"us_per_step": round(start.elapsed_time(stop) * 1e3 / steps, 2),
+            "host_enqueue_us_per_step": round(1e6 * t_enq / steps, 2),
+            "classes": sorted({c for _, c in graphs}), "partition_tokens": stats["partition_tokens"],
+            "attention_workgroups": stats["attention_workgroups"]}
 
 
 def make_workload(name):
@@ -607,6 +673,20 @@ def main():
         "roofline": roof,
         "hbm_reference": hbm_ref,
     }
+    if fused and not args.no_graph:
+        # the same step replayed from captured graphs, at the partition length
+        # the eager calls used (no shared-prefix pass in graph steps)
+        print("bench: graph-replayed steps", file=sys.stderr, flush=True)
+        g_pt = pt if pt > 0 else (pt_used or 0)
+        try:
+            gs = graph_steps(reps, stream, args.steps, args.warmup, g_pt)
+            gs.update({"eager_us_per_step": line["us_per_step"],
+                       "eager_host_enqueue_us_per_step": line["host_enqueue_us_per_step"],
+                       "calls": "pa_graph_prepare, then replay of the graph captured from pa_graph_launch",
+                       "timing": "HIP events on the stream around the timed steps (metadata copies included)"})
+        except abi.PaError as exc:
+            gs = {"error": str(exc)}
+        line["graph_step"] = gs
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, cd, scales)

@@ -1366,6 +1366,9 @@ void attn_append_kernel(AttnParams p, InlineMeta im) {
       a.n_tab = meta[kGraphTab];
       a.n_len = meta[kGraphLen];
       a.n_rows = meta[kGraphRows];
+      a.slots = meta[kGraphSlotsAt];
+      a.tab = meta[kGraphTabAt];
+      a.lens = meta[kGraphLenAt];
       append_work<Q8 ? 1 : static_cast<int>(sizeof(T))>(a, meta, b - n_grid, 64);
       return;
     }

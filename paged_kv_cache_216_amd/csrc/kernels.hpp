@@ -148,9 +148,12 @@ struct AttnParams {
   int graph_units;
 };
 
-// Head of a graph step's metadata: the units of this step, and the table
-// updates, length updates and new rows of its append.
-constexpr int kGraphUnits = 0, kGraphTab = 1, kGraphLen = 2, kGraphRows = 3, kGraphHeader = 8;
+// Head of a graph step's metadata: the units of this step; the table
+// updates, length updates and new rows of its append; where in the metadata
+// its slots, table updates and length updates start.  The lengths by row
+// follow the head.
+constexpr int kGraphUnits = 0, kGraphTab = 1, kGraphLen = 2, kGraphRows = 3, kGraphSlotsAt = 4, kGraphTabAt = 5,
+              kGraphLenAt = 6, kGraphHeader = 8;
 
 constexpr int kInlineMergeParts = 16;
 

@@ -78,13 +78,18 @@ struct PrefixGroup {
 // per sequence): a device buffer holding the step's metadata and its plan,
 // the in-launch merge counters, and the launch parameters, which point at
 // them and so stay the same from step to step.
+// Device buffers of one class of graph steps (units padded to a power of
+// two, rows appended per sequence): the step's own words -- a header, then the
+// lengths by row, the slots, the table and length updates, packed -- and, at
+// fixed offsets after room for the largest such step, the plan (units, then
+// merges).  `plan` is the plan last written there.
 struct GraphClass {
-  void* buf = nullptr;
+  int32_t* buf = nullptr;
   unsigned* ctr = nullptr;
   pa::AttnParams params{};
   int units = 0, n_new = 0;
-  size_t tab_cap = 0, words = 0;
-  size_t off_lens = 0, off_slots = 0, off_tab = 0, off_len = 0, off_units = 0, off_merges = 0;
+  size_t tab_cap = 0, step_words = 0, words = 0, off_units = 0, off_merges = 0;
+  std::vector<int32_t> plan;
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -945,15 +950,12 @@ int ensure_graph_class(pa_pool* p, int units, int n_new, GraphClass** out) {
     const size_t c = static_cast<size_t>(units);
     // table entries a sequence's append can open: one per 16 rows, plus one
     g.tab_cap = c * (static_cast<size_t>(n_new) / pa::kBlock + 2);
-    auto up8 = [](size_t x) { return (x + 7) / 8 * 8; };
-    g.off_lens = pa::kGraphHeader;
-    g.off_slots = up8(g.off_lens + c);
-    g.off_tab = up8(g.off_slots + c * n_new);
-    g.off_len = up8(g.off_tab + 2 * g.tab_cap);
-    g.off_units = up8(g.off_len + 2 * c);
+    // header, lengths by row, slots, table updates, length updates
+    g.step_words = pa::kGraphHeader + c + c * n_new + 2 * g.tab_cap + 2 * c;
+    g.off_units = (g.step_words + 7) / 8 * 8;
     g.off_merges = g.off_units + 8 * c;
     g.words = g.off_merges + 4 * c;
-    hipError_t e = hipMalloc(&g.buf, g.words * sizeof(int32_t));
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(&g.buf), g.words * sizeof(int32_t));
     if (e == hipSuccess) e = hipMalloc(&g.ctr, c * p->hkv * sizeof(unsigned));
     if (e == hipSuccess) e = hipMemset(g.ctr, 0, c * p->hkv * sizeof(unsigned));
     if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -1014,9 +1016,18 @@ int graph_prepare(pa_pool* p, const int32_t* seq_ids, int n_seq, int n_new, cons
   p->pre_groups.clear();
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
 
-  // changes made since the last call reach the device first, eagerly
-  int rc = flush_dirty(p, stream);
-  if (rc != PA_OK) return rc;
+  // Earlier table changes reach the device first, eagerly (the attention
+  // reads the table while the step's append work writes it).  Earlier length
+  // changes (truncations) ride in the step's metadata, as in a fused eager
+  // call, when its class has room for them beside the step's own.
+  int64_t units_est = 0;
+  for (int i = 0; i < n_seq; ++i) units_est += p->parts[i];
+  const int cls = graph_class_units(static_cast<int>(std::min<int64_t>(units_est, int64_t{1} << 29)));
+  int rc = PA_OK;
+  if (p->bp.dirty_entries() > 0 || p->bp.dirty_lens() + static_cast<size_t>(n_seq) > static_cast<size_t>(cls)) {
+    rc = flush_dirty(p, stream);
+    if (rc != PA_OK) return rc;
+  }
   p->ntok.assign(n_seq, n_new);
   p->slots.clear();
   p->cows.clear();
@@ -1041,38 +1052,65 @@ int graph_prepare(pa_pool* p, const int32_t* seq_ids, int n_seq, int n_new, cons
   const size_t n_tab = eager_append ? 0 : d.table_idx.size();
   const size_t n_len = eager_append ? 0 : d.len_seq.size();
   const size_t n_rows = eager_append ? 0 : p->slots.size();
-  if (n_tab > g->tab_cap) return set_err(PA_ERR_STATE, "graph step: more table updates than its class holds");
+  // (the append opens at most n_new / 16 + 1 blocks per sequence, the class
+  // holds n_new / 16 + 2; the lengths were bounded above)
+  if (n_tab > g->tab_cap || n_len > static_cast<size_t>(g->units) || units != units_est ||
+      pa::kGraphHeader + n_seq + n_rows + 2 * (n_tab + n_len) > g->step_words)
+    return set_err(PA_ERR_STATE, "graph step: internal capacity check failed");
 
-  // the step's metadata and plan, in the class's layout
+  // The step's own words, written by small kernels on the stream (their
+  // arguments carry them: no copy engine, no host memory read by the GPU).
   std::vector<int32_t>& w = p->meta;
-  w.assign(g->words, 0);
+  const size_t at_slots = pa::kGraphHeader + static_cast<size_t>(n_seq);
+  const size_t at_tab = at_slots + n_rows, at_len = at_tab + 2 * n_tab, n_words = at_len + 2 * n_len;
+  w.assign(n_words, 0);
   w[pa::kGraphUnits] = units;
   w[pa::kGraphTab] = static_cast<int32_t>(n_tab);
   w[pa::kGraphLen] = static_cast<int32_t>(n_len);
   w[pa::kGraphRows] = static_cast<int32_t>(n_rows);
-  for (int i = 0; i < n_seq; ++i) w[g->off_lens + i] = p->lens[i];
-  for (size_t r = 0; r < n_rows; ++r) w[g->off_slots + r] = p->slots[r];
+  w[pa::kGraphSlotsAt] = static_cast<int32_t>(at_slots);
+  w[pa::kGraphTabAt] = static_cast<int32_t>(at_tab);
+  w[pa::kGraphLenAt] = static_cast<int32_t>(at_len);
+  for (int i = 0; i < n_seq; ++i) w[pa::kGraphHeader + i] = p->lens[i];
+  for (size_t r = 0; r < n_rows; ++r) w[at_slots + r] = p->slots[r];
   for (size_t i = 0; i < n_tab; ++i) {
-    w[g->off_tab + 2 * i] = d.table_idx[i];
-    w[g->off_tab + 2 * i + 1] = d.table_val[i];
+    w[at_tab + 2 * i] = d.table_idx[i];
+    w[at_tab + 2 * i + 1] = d.table_val[i];
   }
   for (size_t i = 0; i < n_len; ++i) {
-    w[g->off_len + 2 * i] = d.len_seq[i];
-    w[g->off_len + 2 * i + 1] = d.len_val[i];
+    w[at_len + 2 * i] = d.len_seq[i];
+    w[at_len + 2 * i + 1] = d.len_val[i];
   }
-  std::memcpy(w.data() + g->off_units, p->units.data(), 8 * p->units.size() * sizeof(int32_t));
-  std::memcpy(w.data() + g->off_merges, p->merges.data(), 4 * p->merges.size() * sizeof(int32_t));
-  Stage* st = nullptr;
-  rc = acquire_stage(p, w.size(), &st);
+  auto put = [&](size_t dst, const int32_t* src, size_t n) -> int {
+    for (size_t done = 0; done < n; done += pa::kInlineWords) {
+      const size_t k = std::min<size_t>(pa::kInlineWords, n - done);
+      std::memcpy(p->inline_meta.w, src + done, k * sizeof(int32_t));
+      hipError_t e = pa::launch_words(g->buf + dst + done, p->inline_meta, static_cast<int>(k), nullptr, 0, stream);
+      if (e != hipSuccess) return hip_err(e, "graph step words");
+    }
+    return PA_OK;
+  };
+  rc = put(0, w.data(), n_words);
   if (rc != PA_OK) return rc;
-  std::memcpy(st->host, w.data(), w.size() * sizeof(int32_t));
-  hipError_t e = hipMemcpyAsync(g->buf, st->host, w.size() * sizeof(int32_t), hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync(graph step)");
-  rc = release_stage(st, stream);
-  if (rc != PA_OK) return rc;
+  // the plan, when it differs from the one the buffer holds (it stays the same
+  // while no sequence of the batch crosses a partition boundary)
+  const size_t unit_words = 8 * p->units.size(), merge_words = 4 * p->merges.size();
+  const int32_t* uw = reinterpret_cast<const int32_t*>(p->units.data());
+  const int32_t* mw = reinterpret_cast<const int32_t*>(p->merges.data());
+  if (g->plan.size() != unit_words + merge_words || !std::equal(uw, uw + unit_words, g->plan.data()) ||
+      !std::equal(mw, mw + merge_words, g->plan.data() + unit_words)) {
+    g->plan.assign(uw, uw + unit_words);
+    g->plan.insert(g->plan.end(), mw, mw + merge_words);
+    rc = put(g->off_units, uw, unit_words);
+    if (rc == PA_OK) rc = put(g->off_merges, mw, merge_words);
+    if (rc != PA_OK) {
+      g->plan.clear();
+      return rc;
+    }
+  }
 
   // launch parameters: the padded grid, pointers into the class's buffer
-  const int32_t* buf = static_cast<const int32_t*>(g->buf);
+  const int32_t* buf = g->buf;
   pa::AttnParams& ak = g->params;
   ak = pa::AttnParams{};
   ak.k_pool = p->k_pool;
@@ -1103,16 +1141,13 @@ int graph_prepare(pa_pool* p, const int32_t* seq_ids, int n_seq, int n_new, cons
   ak.scale_log2 = scale * 1.4426950408889634f;
   ak.stream_kv = 1;  // (a hint only: shared blocks are read correctly either way)
   ak.t_new = n_new;
-  ak.lens_by_row = static_cast<int>(g->off_lens);
+  ak.lens_by_row = pa::kGraphHeader;
   ak.merge_ctr = g->ctr;
   ak.inline_merge = 1;
   ak.kv_scale = p->kv_scale;
   ak.graph_units = g->units;
   ak.app = base_append(p);
-  ak.app.ext = buf;
-  ak.app.tab = static_cast<int>(g->off_tab);
-  ak.app.lens = static_cast<int>(g->off_len);
-  ak.app.slots = static_cast<int>(g->off_slots);
+  ak.app.ext = buf;  // (the offsets of the append's words come from the step's header)
   ak.app.k_new = k_new;
   ak.app.v_new = v_new;
   // the grid's append part: what the class's largest append needs

@@ -8,7 +8,8 @@ twin pool bit for bit (outputs, lse), both pools and their tables must equal
 the oracle's model, and the outputs must match the oracle.  The steps cross
 block boundaries (table updates in the step's metadata), change class (a
 second graph), come back to the first class, and include a copy-on-write
-fork (the append then runs eagerly and the replay only attends).  Capture and
+fork (the append then runs eagerly and the replay only attends), and
+truncations between steps.  Capture and
 replay of launches with in-place updated data, padded to batch classes:
 "CUDA Graphs, modèles de raisonnement et service désagrégé", section 1.
 """
@@ -70,6 +71,12 @@ def test_graph_steps_replay_like_eager_calls(dtype, g, n_new):
             for pr in pairs:
                 pr.alloc(20, 15, int(pr.model.length(15)) - 5)
             forked = True
+        if step in (1, 6):
+            # truncations before a step: their length changes ride in the
+            # step's metadata (sequence 13 is not in the first phase's steps)
+            for pr in pairs:
+                pr.truncate(2, int(pr.model.length(2)) - 3)
+                pr.truncate(13, int(pr.model.length(13)) - 2)
         key = (n, n_new)
         if key not in bufs:
             bufs[key] = _buffers(n, n_new, w, dtype)
