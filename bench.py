@@ -602,8 +602,12 @@ def main():
     D, hkv = w.head_dim, w.num_kv_heads
     prefix_kv_b = stats["prefix_kv_tokens"] * hkv * D * 2 * kv_eb
     prefix_b = prefix_kv_b + stats["prefix_query_rows"] * hkv * D * e if stats["prefix_workgroups"] else 0
-    own = {3: ("prefix_kernel", prefix_b), 0: (attn_name, dec_b - prefix_kv_b + (app_b if fused else 0)),
-           2: ("append_kernel", app_b), 1: ("merge_kernel", 0)}
+    attn_b = dec_b - prefix_kv_b + (app_b if fused else 0)
+    if prefix_b and not kern[3][1] and kern[0][1]:
+        # the shared-prefix units ran inside the attention launch: it moves
+        # the whole step's bytes (the prefix once, q once)
+        attn_name, attn_b = "attn_prefix_kernel", dec_b + (app_b if fused else 0)
+    own = {3: ("prefix_kernel", prefix_b), 0: (attn_name, attn_b), 2: ("append_kernel", app_b), 1: ("merge_kernel", 0)}
     kernels, kernel_us_step, traffic = [], 0.0, 0
     for k in (3, 2, 0, 1):
         ms, n = kern[k]

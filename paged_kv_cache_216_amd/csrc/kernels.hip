@@ -760,14 +760,18 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
         const int bytes1 = j + 1 < cnt ? kPageBytes : 0;
         const size_t off0 = (static_cast<size_t>(phys_at(min(j, cnt - 1))) * p.hkv + kvh) * page;
         const size_t off1 = (static_cast<size_t>(phys_at(min(j + 1, cnt - 1))) * p.hkv + kvh) * page;
-        const __amdgpu_buffer_rsrc_t rs[4] = {page_rsrc(kpool + off0, bytes0), page_rsrc(kpool + off1, bytes1),
-                                              page_rsrc(vpool + off0, bytes0), page_rsrc(vpool + off1, bytes1)};
+        const auto rk0 = page_rsrc(kpool + off0, bytes0), rk1 = page_rsrc(kpool + off1, bytes1);
+        const auto rv0 = page_rsrc(vpool + off0, bytes0), rv1 = page_rsrc(vpool + off1, bytes1);
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
           const int c0 = wave * 64 + 64 * W * k;  // first chunk of the wave's 64
           const int pg = c0 / kChunksPerPage;
+          // the page's descriptor by uniform selects (an indexed array of
+          // descriptors would be moved to vector registers and read back by
+          // a loop over the lanes)
+          const auto rs = pg == 0 ? rk0 : pg == 1 ? rk1 : pg == 2 ? rv0 : rv1;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rs[pg], (__attribute__((address_space(3))) void*)(&lds[b][c0 * 16]), 16,
+              rs, (__attribute__((address_space(3))) void*)(&lds[b][c0 * 16]), 16,
               (c0 - pg * kChunksPerPage + lane) * 16, 0, 0, NTL ? 2 : 0);
         }
       };

@@ -871,7 +871,11 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   ak.tile_rows = pa::tile_rows_for_call(p->dtype, p->head_dim, rows);
   ak.head_dim = p->head_dim;
   ak.scale_log2 = scale * 1.4426950408889634f;
-  ak.stream_kv = (p->bp.num_shared() == 0 && !pre_in_launch) ? 1 : 0;
+  // Pages stream past the caches (non-temporal loads) only when one unit
+  // reads each of them: no shared blocks, no shared-prefix units, and one
+  // row tile per (sequence, partition).  The row tiles of a long chunk read
+  // the same pages one after the other and find them in L2.
+  ak.stream_kv = (p->bp.num_shared() == 0 && !pre_in_launch && ak.tile_rows >= rows) ? 1 : 0;
   ak.app = base_append(p);
   // Short splits (few partitions, one row tile) are merged inside the
   // attention launch by the last partition to finish; others by merge_kernel.
@@ -1023,7 +1027,11 @@ int graph_prepare(pa_pool* p, const int32_t* seq_ids, int n_seq, int n_new, cons
   int64_t units_est = 0;
   for (int i = 0; i < n_seq; ++i) units_est += p->parts[i];
   const int cls = graph_class_units(static_cast<int>(std::min<int64_t>(units_est, int64_t{1} << 29)));
-  int rc = PA_OK;
+  // the class's buffers first: nothing after the append's bookkeeping may fail
+  // but a launch
+  GraphClass* g = nullptr;
+  int rc = ensure_graph_class(p, cls, n_new, &g);
+  if (rc != PA_OK) return rc;
   if (p->bp.dirty_entries() > 0 || p->bp.dirty_lens() + static_cast<size_t>(n_seq) > static_cast<size_t>(cls)) {
     rc = flush_dirty(p, stream);
     if (rc != PA_OK) return rc;
@@ -1045,9 +1053,6 @@ int graph_prepare(pa_pool* p, const int32_t* seq_ids, int n_seq, int n_new, cons
   make_plan(p, seq_ids, n_seq, pt, rows, group, n_new, false);
   p->plan_key.clear();  // the pool's own plan cache no longer matches its host plan
   const int units = static_cast<int>(p->units.size());
-  GraphClass* g = nullptr;
-  rc = ensure_graph_class(p, graph_class_units(units), n_new, &g);
-  if (rc != PA_OK) return rc;
   const pa::BlockPool::Dirty& d = p->dirty;
   const size_t n_tab = eager_append ? 0 : d.table_idx.size();
   const size_t n_len = eager_append ? 0 : d.len_seq.size();
