@@ -211,7 +211,9 @@ int pa_append_kv(pa_pool* pool, const int32_t* seq_ids, int n_seq, const int32_t
  *   seq_ids      host int32 [n_seq]; live, length >= 1 (repeats allowed)
  *   num_q_heads  multiple of num_kv_heads; query head h reads key/value head
  *                h / (num_q_heads / num_kv_heads)
- *   scale        multiplies q.k before the softmax (typically 1/sqrt(head_dim))
+ *   scale        multiplies q.k before the softmax (typically 1/sqrt(head_dim));
+ *                finite and > 0, else PA_ERR_INVALID (the same for every
+ *                attention call below)
  *   q, out       device [n_seq][num_q_heads][head_dim] in dtype
  *   lse          device float [n_seq][num_q_heads] (natural-log log-sum-exp of
  *                the scaled scores) or NULL

@@ -239,12 +239,18 @@ struct MfmaOp<_Float16> {
   }
 };
 
+// Maximum of floats as gfx950's v_maximum3_f32 takes it: NaN-propagating, so
+// no operand needs quieting first (fmaxf costs a canonicalizing v_max per
+// operand in IEEE mode).  Scores of valid tokens are finite; masked ones are
+// -inf before any maximum.
+__device__ inline float fmax_prop(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ inline float wave_max_groups(float x) {
   // max over lanes col, col+16, col+32, col+48
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = fmax_prop(__uint_as_float(a[0]), __uint_as_float(a[1]));
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return fmax_prop(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ inline float wave_sum_groups(float x) {
@@ -600,11 +606,13 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
         s0 = MfmaOp<T>::mma(f.k0[s], qop[nt][s], s0);
         s1 = MfmaOp<T>::mma(f.k1[s], qop[nt][s], s1);
       }
+      // raw scores: the scale (> 0) goes into the maximum once per row and into
+      // each exponent's fused multiply-add
       float x[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[e] = s0[e] * sl2;
-        x[4 + e] = s1[e] * sl2;
+        x[e] = s0[e];
+        x[4 + e] = s1[e];
       }
       if (need_mask) {
 #pragma unroll
@@ -616,8 +624,9 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       }
       float mt = x[0];
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
-      mt = wave_max_groups(mt);
+      for (int e = 1; e < 8; ++e) mt = fmax_prop(mt, x[e]);
+      // (scaling by sl2 > 0 commutes with the maximum, rounding included)
+      mt = wave_max_groups(mt) * sl2;
       // The reference maximum of a row moves only when a score exceeds it by
       // more than kMaxSlack (log2 units), so probabilities stay <= 2^kMaxSlack:
       // exact in real arithmetic (acc, l and m stay consistent), no precision
@@ -630,7 +639,7 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       float ps = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(x[e] - m_use);
+        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], sl2, -m_use));
         ps += pe;
         pa[nt][e] = static_cast<T>(pe);
       }
@@ -748,31 +757,33 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       constexpr int kChunksPerPage = kPageBytes / 16;
       constexpr int kRing = 3;
       static_assert(kPer * 16 * 64 * W == kPair, "pair image must split evenly");
-      static_assert(kChunksPerPage % 64 == 0, "a wave's 64 chunks lie in one page");
+      static_assert(kChunksPerPage == 64 * kPer, "a wave's loads cover one page");
       static_assert(kRing >= 2 && kRing <= 4 && (kRing - 2) * kPer <= 63, "the waits below cover up to two later pairs");
       __shared__ __attribute__((aligned(16))) char lds[kRing][kPair];
+      static_assert(W == 4, "one wave per page of the pair image");
       const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-      // each load instruction fills 64 consecutive 16-byte chunks of one page:
-      // lane l writes chunk c0 + l (the LDS address is the wave's base plus 16 l)
+      // Wave w loads page w of the image (K of the pair's first block, K of
+      // its second, then their V), so it builds one buffer descriptor per
+      // pair; each load instruction fills 64 consecutive 16-byte chunks of
+      // that page (lane l writes chunk c0 + l: the LDS address is the wave's
+      // base plus 16 l).
+      const bool v_page = wave >= 2;
+      const auto* wpool = v_page ? vpool : kpool;
       auto dma = [&](int pj, int b) {
-        const int j = 2 * pj;
-        const int bytes0 = j < cnt ? kPageBytes : 0;
-        const int bytes1 = j + 1 < cnt ? kPageBytes : 0;
-        const size_t off0 = (static_cast<size_t>(phys_at(min(j, cnt - 1))) * p.hkv + kvh) * page;
-        const size_t off1 = (static_cast<size_t>(phys_at(min(j + 1, cnt - 1))) * p.hkv + kvh) * page;
-        const auto rk0 = page_rsrc(kpool + off0, bytes0), rk1 = page_rsrc(kpool + off1, bytes1);
-        const auto rv0 = page_rsrc(vpool + off0, bytes0), rv1 = page_rsrc(vpool + off1, bytes1);
+        const int j = 2 * pj + (wave & 1);
+        const int bytes = j < cnt ? kPageBytes : 0;
+        const size_t off = (static_cast<size_t>(phys_at(min(j, cnt - 1))) * p.hkv + kvh) * page;
+        const auto rs = page_rsrc(wpool + off, bytes);
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
-          const int c0 = wave * 64 + 64 * W * k;  // first chunk of the wave's 64
-          const int pg = c0 / kChunksPerPage;
-          // the page's descriptor by uniform selects (an indexed array of
-          // descriptors would be moved to vector registers and read back by
-          // a loop over the lanes)
-          const auto rs = pg == 0 ? rk0 : pg == 1 ? rk1 : pg == 2 ? rv0 : rv1;
+          const int lc = 64 * k + lane;  // this lane's chunk of the page
+          // V pages (16-bit): LDS chunk h * D + d holds the pool's chunk
+          // (dim d, tokens 8h .. 8h + 7), so that the 16 lanes of a fragment
+          // read (16 dims, one token half) sit 16 bytes apart, not 32
+          const int gc = (!Q8 && v_page) ? (lc % D) * 2 + lc / D : lc;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rs, (__attribute__((address_space(3))) void*)(&lds[b][c0 * 16]), 16,
-              (c0 - pg * kChunksPerPage + lane) * 16, 0, 0, NTL ? 2 : 0);
+              rs, (__attribute__((address_space(3))) void*)(&lds[b][(wave * kChunksPerPage + 64 * k) * 16]), 16,
+              gc * 16, 0, 0, NTL ? 2 : 0);
         }
       };
       auto lfrag = [&](Frag& f, int b) {
@@ -801,7 +812,7 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
           }
 #pragma unroll
           for (int c = 0; c < DC; ++c) {
-            const int o = ((16 * c + col) * kBlk + 4 * grp) * 2;
+            const int o = ((grp >> 1) * D + 16 * c + col) * 16 + 8 * (grp & 1);
             f.v0[c] = *reinterpret_cast<const u32x2*>(vb + o);
             f.v1[c] = *reinterpret_cast<const u32x2*>(vb + kPageBytes + o);
           }

@@ -661,6 +661,7 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   if (k_draft < 1) return set_err(PA_ERR_INVALID, "k_draft must be >= 1");
   if (num_q_heads <= 0 || num_q_heads % p->hkv != 0)
     return set_err(PA_ERR_INVALID, "num_q_heads must be a positive multiple of num_kv_heads");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return set_err(PA_ERR_INVALID, "scale must be finite and > 0");
   const int group = num_q_heads / p->hkv;
   const int64_t rows64 = static_cast<int64_t>(group) * k_draft;
   if (rows64 > kMaxRows)
@@ -989,6 +990,7 @@ int graph_prepare(pa_pool* p, const int32_t* seq_ids, int n_seq, int n_new, cons
   if (!seq_ids || !q || !out || !k_new || !v_new) return set_err(PA_ERR_INVALID, "NULL argument");
   if (num_q_heads <= 0 || num_q_heads % p->hkv != 0)
     return set_err(PA_ERR_INVALID, "num_q_heads must be a positive multiple of num_kv_heads");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return set_err(PA_ERR_INVALID, "scale must be finite and > 0");
   const int group = num_q_heads / p->hkv;
   const int64_t rows64 = static_cast<int64_t>(group) * n_new;
   if (rows64 > rows_limit(p))
