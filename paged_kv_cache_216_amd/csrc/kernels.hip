@@ -372,79 +372,130 @@ __device__ inline f32x4 load_device4(__amdgpu_buffer_rsrc_t r, int byte_off) {
 // write back and invalidate the whole L2 of the XCD around the atomic:
 // measured on MI355X, batch-256 decode 64 -> 95 us and the 70B-like decode
 // 54 -> 97 us with an acq_rel increment.
-template <typename T, int D>
-__device__ inline void merge_last(const AttnParams& p, int merge, int kvh) {
+// The merge of one split (sequence, kv head): RG groups of 4 rows per pass,
+// each lane taking 16-byte column chunks of one row of a group, the loads of
+// all RG groups' partitions issued together; partitions C at a time,
+// combined with a running maximum (one chunk: M = max m_q, the weights
+// 2^(m_q - M)).  Chunks past the sequence's partitions weigh 0.
+template <typename T, int D, int C, int RG>
+__device__ inline void merge_rows(const AttnParams& p, const MergeUnit& mu, int kvh, int lane, int r_begin,
+                                  int r_end) {
   constexpr int V = D / 64;  // 16-byte column chunks per lane
-  constexpr int C = 8;       // partitions loaded at once
-  const int lane = threadIdx.x & 63;
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores have completed
-  const MergeUnit mu = p.merges[merge];
-  unsigned* ctr = p.merge_ctr + merge * p.hkv + kvh;
-  unsigned old = 0;
-  if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  old = __builtin_amdgcn_readfirstlane(old);
-  if (old != static_cast<unsigned>(mu.arrivals - 1)) return;  // (earlier partitions: a previous launch)
-  // every arrival has counted itself: reset for the next launch, then merge
-  if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int P = mu.nparts;
-  const int rows = p.rows;
+  const int rows = r_end;  // rows past r_end repeat row r_end - 1 and are not stored
   const int base = mu.slot_base + kvh * P;
   const auto racc = page_rsrc(p.ws_acc, 0x7ffffff0);
   const int c0 = (lane & 15) * (D / 16);
-  for (int r0 = 0; r0 < rows; r0 += 4) {
-    const int r = r0 + (lane >> 4);
-    const int rr = r < rows ? r : rows - 1;
-    // partitions C at a time, combined with a running maximum (one chunk:
-    // M = max m_q, the weights 2^(m_q - M))
-    float M = kNegInf, den = 0.f;
-    f32x4 num[V];
+  for (int r0 = r_begin; r0 < rows; r0 += 4 * RG) {
+    int r[RG], rr[RG];
+    float M[RG], den[RG];
+    f32x4 num[RG][V];
 #pragma unroll
-    for (int v = 0; v < V; ++v) num[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < RG; ++g) {
+      r[g] = r0 + 4 * g + (lane >> 4);
+      rr[g] = r[g] < rows ? r[g] : rows - 1;
+      M[g] = kNegInf;
+      den[g] = 0.f;
+#pragma unroll
+      for (int v = 0; v < V; ++v) num[g][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     for (int q0 = 0; q0 < P; q0 += C) {
-      float m[C], l[C];
-      f32x4 a[C][V];
+      float m[RG][C], l[RG][C];
+      f32x4 a[RG][C][V];
 #pragma unroll
-      for (int q = 0; q < C; ++q) {
-        const int qq = min(q0 + q, P - 1);
-        const size_t sl = static_cast<size_t>(base + qq) * rows + rr;
-        m[q] = load_device(p.ws_ml + 2 * sl);
-        l[q] = load_device(p.ws_ml + 2 * sl + 1);
+      for (int g = 0; g < RG; ++g)
 #pragma unroll
-        for (int v = 0; v < V; ++v) a[q][v] = load_device4(racc, static_cast<int>((sl * D + c0 + 4 * v) * 4));
-      }
-      float Mn = M;
+        for (int q = 0; q < C; ++q) {
+          const int qq = min(q0 + q, P - 1);
+          const size_t sl = static_cast<size_t>(base + qq) * p.rows + rr[g];
+          m[g][q] = load_device(p.ws_ml + 2 * sl);
+          l[g][q] = load_device(p.ws_ml + 2 * sl + 1);
 #pragma unroll
-      for (int q = 0; q < C; ++q) Mn = q0 + q < P ? fmaxf(Mn, m[q]) : Mn;
-      const float mu_ = (Mn == kNegInf) ? 0.f : Mn;
-      const float so = __builtin_amdgcn_exp2f(M - mu_);  // 0 on the first chunk
-      den *= so;
+          for (int v = 0; v < V; ++v) a[g][q][v] = load_device4(racc, static_cast<int>((sl * D + c0 + 4 * v) * 4));
+        }
 #pragma unroll
-      for (int v = 0; v < V; ++v)
+      for (int g = 0; g < RG; ++g) {
+        float Mn = M[g];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) num[v][e] *= so;
-#pragma unroll
-      for (int q = 0; q < C; ++q) {
-        const float w = q0 + q < P ? __builtin_amdgcn_exp2f(m[q] - mu_) : 0.f;
-        den += w * l[q];
+        for (int q = 0; q < C; ++q) Mn = q0 + q < P ? fmaxf(Mn, m[g][q]) : Mn;
+        const float mu_ = (Mn == kNegInf) ? 0.f : Mn;
+        const float so = __builtin_amdgcn_exp2f(M[g] - mu_);  // 0 on the first chunk
+        den[g] *= so;
 #pragma unroll
         for (int v = 0; v < V; ++v)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) num[v][e] += w * a[q][v][e];
+          for (int e = 0; e < 4; ++e) num[g][v][e] *= so;
+#pragma unroll
+        for (int q = 0; q < C; ++q) {
+          const float w = q0 + q < P ? __builtin_amdgcn_exp2f(m[g][q] - mu_) : 0.f;
+          den[g] += w * l[g][q];
+#pragma unroll
+          for (int v = 0; v < V; ++v)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) num[g][v][e] += w * a[g][q][v][e];
+        }
+        M[g] = Mn;
       }
-      M = Mn;
     }
-    if (r < rows) {
-      const int i = r / p.group, g = r - (r / p.group) * p.group;
-      const size_t orow = static_cast<size_t>(mu.q_row * p.k_draft + i) * p.hq + kvh * p.group + g;
-      const float inv = 1.f / den;
-      T* op = static_cast<T*>(p.out) + orow * D + c0;
 #pragma unroll
-      for (int v = 0; v < V; ++v)
+    for (int g = 0; g < RG; ++g) {
+      if (r[g] < rows) {
+        const int i = r[g] / p.group, gg = r[g] - (r[g] / p.group) * p.group;
+        const size_t orow = static_cast<size_t>(mu.q_row * p.k_draft + i) * p.hq + kvh * p.group + gg;
+        const float inv = 1.f / den[g];
+        T* op = static_cast<T*>(p.out) + orow * D + c0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) store_elem(op + 4 * v + e, num[v][e] * inv);
-      if ((lane & 15) == 0 && p.lse) p.lse[orow] = (M + __builtin_amdgcn_logf(den)) * kLn2;
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) store_elem(op + 4 * v + e, num[g][v][e] * inv);
+        if ((lane & 15) == 0 && p.lse) p.lse[orow] = (M[g] + __builtin_amdgcn_logf(den[g])) * kLn2;
+      }
     }
   }
+}
+
+// Rows [r_begin, r_end) of a split (sequence, kv head), in the shape that
+// fits them.  (The same arithmetic in every shape: chunks of C = 8
+// partitions, or one chunk of 4 when there are at most 4, where the chunk of
+// 8 would add zero weights only.)
+template <typename T, int D>
+__device__ inline void merge_rows_of(const AttnParams& p, const MergeUnit& mu, int kvh, int lane, int r_begin,
+                                     int r_end) {
+  if (r_end - r_begin <= 4) {
+    if (mu.nparts <= 4)
+      merge_rows<T, D, 4, 1>(p, mu, kvh, lane, r_begin, r_end);
+    else
+      merge_rows<T, D, 8, 1>(p, mu, kvh, lane, r_begin, r_end);
+  } else if (mu.nparts <= 4) {
+    merge_rows<T, D, 4, 4>(p, mu, kvh, lane, r_begin, r_end);
+  } else if (mu.nparts <= 8) {
+    merge_rows<T, D, 8, 2>(p, mu, kvh, lane, r_begin, r_end);
+  } else {
+    merge_rows<T, D, 8, 1>(p, mu, kvh, lane, r_begin, r_end);
+  }
+}
+
+// One arrival at split (merge, kvh), counted by the calling lane after its
+// wave's (or workgroup's) partial stores have completed; true for the last
+// arrival, which also resets the counter for the next launch.
+__device__ inline bool merge_arrive(const AttnParams& p, int merge, int kvh) {
+  unsigned* ctr = p.merge_ctr + merge * p.hkv + kvh;
+  const unsigned old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // (earlier partitions: a previous launch)
+  if (old != static_cast<unsigned>(p.merges[merge].arrivals - 1)) return false;
+  __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+template <typename T, int D>
+__device__ inline void merge_last(const AttnParams& p, int merge, int kvh) {
+  const int lane = threadIdx.x & 63;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores have completed
+  bool last = false;
+  if (lane == 0) last = merge_arrive(p, merge, kvh);
+  if (!__builtin_amdgcn_readfirstlane(static_cast<int>(last))) return;
+  // every arrival has counted itself: merge
+  merge_rows_of<T, D>(p, p.merges[merge], kvh, lane, 0, p.rows);
 }
 
 // Largest amount (log2 domain) by which a score may exceed its row's
@@ -755,7 +806,7 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       constexpr int kPair = 4 * kPageBytes;
       constexpr int kPer = kPair / (16 * 64 * W);  // 16-byte chunks per thread
       constexpr int kChunksPerPage = kPageBytes / 16;
-      constexpr int kRing = 3;
+      constexpr int kRing = 4;
       static_assert(kPer * 16 * 64 * W == kPair, "pair image must split evenly");
       static_assert(kChunksPerPage == 64 * kPer, "a wave's loads cover one page");
       static_assert(kRing >= 2 && kRing <= 4 && (kRing - 2) * kPer <= 63, "the waits below cover up to two later pairs");
@@ -1054,14 +1105,12 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
         }
       }
     }
-    if constexpr (W == 1) {
-      if (dev) {
-        // every member whose rows this wave holds: count this arrival, and
-        // the last arrival merges the member
-        const int r_end = min(u.pre_row0 + 16 * NT, u.pre_rows);
-        for (int j = u.pre_row0 / rows; j * rows < r_end; ++j)
-          merge_last<T, D>(p, p.pre_members[u.pre_member0 + j].merge, kvh);
-      }
+    if (dev && u.pre_row0 < u.pre_rows) {
+      // every member whose rows this wave holds: count this arrival, and the
+      // last arrival merges the member
+      const int r_end = min(u.pre_row0 + 16 * NT, u.pre_rows);
+      for (int j = u.pre_row0 / rows; j * rows < r_end; ++j)
+        merge_last<T, D>(p, p.pre_members[u.pre_member0 + j].merge, kvh);
     }
     return;
   }
@@ -1291,9 +1340,9 @@ __device__ inline void attn_body32(const AttnParams& p, const Unit& u, int kvh) 
 
 // One workgroup (one wave) per (work unit, key/value head).
 template <typename T, int D, int NT, bool NTL, bool FUSED, bool Q8 = false, bool ONE_PAIR = false>
-__device__ inline void attn_unit(const AttnParams& p, const int32_t* meta) {
-  const int unit = blockIdx.x / p.hkv;
-  const int kvh = blockIdx.x - unit * p.hkv;
+__device__ inline void attn_unit(const AttnParams& p, const int32_t* meta, int block) {
+  const int unit = block / p.hkv;
+  const int kvh = block - unit * p.hkv;
   const WorkUnit w = p.units[unit];
   Unit u;
   u.q_row = w.q_row;
@@ -1322,7 +1371,7 @@ __device__ inline void attn_unit(const AttnParams& p, const int32_t* meta) {
 
 template <typename T, int D, int NT, bool NTL, bool Q8 = false>
 __global__ __launch_bounds__(64) void attn_kernel(AttnParams p) {
-  attn_unit<T, D, NT, NTL, false, Q8>(p, nullptr);
+  attn_unit<T, D, NT, NTL, false, Q8>(p, nullptr, blockIdx.x);
 }
 
 // Many query rows per (sequence, kv head) -- chunked prefill, long verify --
@@ -1388,7 +1437,7 @@ void attn_append_kernel(AttnParams p, InlineMeta im) {
       return;
     }
     if (b >= meta[kGraphUnits] * p.hkv) return;
-    attn_unit<T, D, NT, NTL, true, Q8>(p, meta);
+    attn_unit<T, D, NT, NTL, true, Q8>(p, meta, blockIdx.x);
     return;
   }
   const int n_attn = p.n_units * p.hkv;
@@ -1396,22 +1445,22 @@ void attn_append_kernel(AttnParams p, InlineMeta im) {
     append_work<Q8 ? 1 : static_cast<int>(sizeof(T))>(p.app, meta, b - n_attn, 64);
     return;
   }
-  attn_unit<T, D, NT, NTL, true, Q8>(p, meta);
+  attn_unit<T, D, NT, NTL, true, Q8>(p, meta, blockIdx.x);
 }
 
 // Shared-prefix pass: one workgroup of W waves per (prefix unit, kv head);
 // wave w takes 16 * NT query rows of one group of sequences over one
-// partition of their common prefix.  (Measured on MI355X, 64-fork verify:
-// for 16-bit pools one wave per workgroup, 2 tiles, one pair in flight and two
-// waves per SIMD is best -- the next pair in flight at one wave per SIMD,
-// several waves reading the same pages, four waves sharing each pair through
-// the LDS ring of the row tiles (48 us against 42 us), or 4 tiles per wave
-// are slower; for E4M3 pools the four-wave LDS ring is best, 43 us against
-// 56 us: the 8-bit pair image is half the size.)
+// partition of their common prefix, the four waves sharing each pair of
+// blocks through the LDS ring of the row tiles.  (Measured on MI355X, 64-fork
+// verify with 16-bit pools: single-wave workgroups with one pair in flight
+// at two waves per SIMD were best while the ring's loads were built with
+// four descriptors per wave and read V with 4-way bank conflicts; with one
+// page per wave and the V image reordered the ring is faster, for E4M3 pools
+// too, whose pair image is half the size.)
 template <int D, bool Q8 = false>
 struct PrefixShape {
   static constexpr int NT = D <= 128 ? 2 : 1;            // row tiles per wave
-  static constexpr int W = Q8 ? 4 : 1;                   // waves per workgroup
+  static constexpr int W = 4;                            // waves per workgroup
   static constexpr int kWavesPerSimd = D <= 128 ? 2 : 1;  // resident waves per SIMD
 };
 
@@ -1453,27 +1502,36 @@ void prefix_kernel(AttnParams p) {
 }
 
 // Attention units, then the shared-prefix units, then (FUSED) the append work,
-// in one launch of single-wave workgroups (16-bit pools): the pass over the
+// in one launch of four-wave workgroups (16-bit pools): the pass over the
 // shared prefix overlaps the members' own partitions, and the last wave to
-// finish partials of a (member, kv head) merges them.  Multi-tile units keep
-// one pair in flight here, so that the launch holds two waves per SIMD as the
-// prefix pass needs.
+// finish partials of a (member, kv head) merges them.  An attention workgroup
+// runs four independent single-wave units (no barrier, no LDS); a prefix
+// workgroup is the pass's four-wave unit.  Multi-tile units keep one pair in
+// flight, so that the launch holds two waves per SIMD as the prefix pass
+// needs.
+constexpr int kPrefixLaunchWaves = 4;
+
 template <typename T, int D, int NT, bool FUSED>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
+__global__ __launch_bounds__(64 * kPrefixLaunchWaves) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
 void attn_prefix_kernel(AttnParams p, InlineMeta im) {
+  static_assert(PrefixShape<D>::W == kPrefixLaunchWaves, "prefix units are the launch's workgroups");
   const int32_t* meta = p.app.ext ? p.app.ext : im.w;
-  const int n_attn = p.n_units * p.hkv;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int n_attn = p.n_units * p.hkv;  // attention waves
+  const int n_attn_wg = (n_attn + kPrefixLaunchWaves - 1) / kPrefixLaunchWaves;
   const int n_pre = p.n_pre_units * p.hkv;
   const int b = blockIdx.x;
-  if (b < n_attn) {
-    attn_unit<T, D, NT, false, FUSED, false, true>(p, meta);
+  if (b < n_attn_wg) {
+    const int vb = b * kPrefixLaunchWaves + wave;
+    if (vb < n_attn) attn_unit<T, D, NT, false, FUSED, false, true>(p, meta, vb);
     return;
   }
-  if (b < n_attn + n_pre) {
-    prefix_unit<T, D, false>(p, b - n_attn);
+  if (b < n_attn_wg + n_pre) {
+    prefix_unit<T, D, false>(p, b - n_attn_wg);
     return;
   }
-  if constexpr (FUSED) append_work<static_cast<int>(sizeof(T))>(p.app, meta, b - n_attn - n_pre, 64);
+  if constexpr (FUSED)
+    append_work<static_cast<int>(sizeof(T))>(p.app, meta, b - n_attn_wg - n_pre, 64 * kPrefixLaunchWaves);
 }
 
 // Exact merge of one output row of a split sequence, one 256-thread workgroup
@@ -1558,11 +1616,14 @@ template <typename T, int D, int NT, bool NTL, bool Q8>
 void launch_attn_nt(const AttnParams& p, const InlineMeta& m, hipStream_t stream) {
   if constexpr (!std::is_same_v<T, float> && !Q8 && !NTL && (D <= 128 ? NT <= 2 : NT == 1)) {
     if (p.pre_in_launch) {
-      const dim3 grid(static_cast<unsigned>(p.n_units + p.n_pre_units) * p.hkv + (p.t_new > 0 ? p.app_blocks : 0));
+      // (app_blocks counts workgroups of the launch's size here)
+      const int attn_wg = (p.n_units * p.hkv + kPrefixLaunchWaves - 1) / kPrefixLaunchWaves;
+      const dim3 grid(static_cast<unsigned>(attn_wg + p.n_pre_units * p.hkv + (p.t_new > 0 ? p.app_blocks : 0)));
+      const dim3 block(64 * kPrefixLaunchWaves);
       if (p.t_new > 0)
-        hipLaunchKernelGGL((attn_prefix_kernel<T, D, NT, true>), grid, dim3(64), 0, stream, p, m);
+        hipLaunchKernelGGL((attn_prefix_kernel<T, D, NT, true>), grid, block, 0, stream, p, m);
       else
-        hipLaunchKernelGGL((attn_prefix_kernel<T, D, NT, false>), grid, dim3(64), 0, stream, p, m);
+        hipLaunchKernelGGL((attn_prefix_kernel<T, D, NT, false>), grid, block, 0, stream, p, m);
       return;
     }
   }
@@ -1700,6 +1761,15 @@ int append_blocks64(const AppendParams& p) {
   const AppendGrid g = append_grid(p, 64);
   return g.upd_blocks + g.cow_blocks + g.row_blocks;
 }
+
+int append_blocks_prefix_launch(const AppendParams& p) {
+  const AppendGrid g = append_grid(p, 64 * kPrefixLaunchWaves);
+  return g.upd_blocks + g.cow_blocks + g.row_blocks;
+}
+
+int prefix_rows_per_wave(int head_dim) { return 16 * (head_dim <= 128 ? PrefixShape<128>::NT : PrefixShape<256>::NT); }
+
+int prefix_launch_waves() { return kPrefixLaunchWaves; }
 
 hipError_t launch_append(const AppendParams& p, const InlineMeta* meta, hipStream_t stream) {
   const AppendGrid g = append_grid(p, kAppendThreads);

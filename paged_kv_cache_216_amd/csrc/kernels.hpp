@@ -173,6 +173,13 @@ bool prefix_in_attention_launch(int dtype, int head_dim, int rows);
 int prefix_units_per_cu(int dtype, int head_dim);
 // Workgroups of 64 threads that the append work of `p` needs.
 int append_blocks64(const AppendParams& p);
+// Workgroups that the append work of `p` needs in the attention launch that
+// also runs the shared-prefix units (pre_in_launch: workgroups of
+// prefix_launch_waves() waves, each running that many attention units).
+int append_blocks_prefix_launch(const AppendParams& p);
+int prefix_launch_waves();
+// Query rows one wave of the shared-prefix pass takes.
+int prefix_rows_per_wave(int head_dim);
 // Query rows one single-wave attention unit takes at most, for a head dim.
 int max_rows_for_head_dim(int head_dim);
 // Query rows per unit for a call with `rows` rows per kv head: all of them when

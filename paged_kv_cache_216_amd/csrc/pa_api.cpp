@@ -394,9 +394,12 @@ void make_plan(pa_pool* p, const int32_t* seq_ids, int n_seq, int pt, int rows, 
       for (int r0 = 0; r0 < group_rows; r0 += rpw) {
         p->pre_units.push_back({seq_ids[first], q, r0, member0, group_rows, shared, 0, 0});
         if (pre_in_launch) {
-          // this wave arrives once for every member whose rows it holds
-          const int r_end = std::min(r0 + rpw, group_rows);
-          for (int j = r0 / rows; j * rows < r_end; ++j) p->merges[merge_of[pairs[a + j].second]].arrivals += 1;
+          // each wave of the unit arrives once for every member whose rows it holds
+          const int wr = pa::prefix_rows_per_wave(p->head_dim);
+          for (int w0 = r0; w0 < std::min(r0 + rpw, group_rows); w0 += wr) {
+            const int r_end = std::min(w0 + wr, group_rows);
+            for (int j = w0 / rows; j * rows < r_end; ++j) p->merges[merge_of[pairs[a + j].second]].arrivals += 1;
+          }
         }
       }
     a = b;
@@ -735,8 +738,10 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
   find_prefix_groups(p, seq_ids, n_seq, pt, k_draft, rows);
   if (partition_tokens == 0 && pt > 0) {
     // the launch's other waves, when the pass runs inside the attention launch
+    // (workgroups of that launch run prefix_launch_waves() attention units each)
+    const int64_t lw = pa::prefix_launch_waves();
     const int64_t others = (pa::prefix_in_attention_launch(p->dtype, p->head_dim, rows) && rows <= rows_limit(p))
-                               ? static_cast<int64_t>(n_seq) * p->hkv
+                               ? (static_cast<int64_t>(n_seq) * p->hkv + lw - 1) / lw
                                : 0;
     const int best = prefix_partition(p, pt, rows, others);
     if (best != pt) {
@@ -899,7 +904,7 @@ int attend(pa_pool* p, const int32_t* seq_ids, int n_seq, int k_draft, int num_q
     ak.app.v_new = app->v_new;
     ak.app.n_rows = static_cast<int>(p->slots.size());
     ak.t_new = t_new;
-    ak.app_blocks = pa::append_blocks64(ak.app);
+    ak.app_blocks = pre_in_launch ? pa::append_blocks_prefix_launch(ak.app) : pa::append_blocks64(ak.app);
     int rc = meta_submit(p, &ak.app.ext, &st);
     if (rc != PA_OK) return rc;
   }

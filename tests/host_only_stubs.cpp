@@ -27,6 +27,9 @@ int prefix_rows_per_unit(int, int) { unreachable("prefix_rows_per_unit"); }
 int prefix_units_per_cu(int, int) { unreachable("prefix_units_per_cu"); }
 bool prefix_in_attention_launch(int, int, int) { unreachable("prefix_in_attention_launch"); }
 int append_blocks64(const AppendParams&) { unreachable("append_blocks64"); }
+int append_blocks_prefix_launch(const AppendParams&) { unreachable("append_blocks_prefix_launch"); }
+int prefix_launch_waves() { unreachable("prefix_launch_waves"); }
+int prefix_rows_per_wave(int) { unreachable("prefix_rows_per_wave"); }
 int max_rows_for_head_dim(int) { unreachable("max_rows_for_head_dim"); }
 int tile_rows_for_call(int, int, int) { unreachable("tile_rows_for_call"); }
 hipError_t launch_swap(const SwapParams&, hipStream_t) { unreachable("launch_swap"); }
