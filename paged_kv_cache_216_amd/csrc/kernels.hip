@@ -1511,10 +1511,10 @@ void prefix_kernel(AttnParams p) {
 // needs.
 constexpr int kPrefixLaunchWaves = 4;
 
-template <typename T, int D, int NT, bool FUSED>
+template <typename T, int D, int NT, bool FUSED, bool Q8>
 __global__ __launch_bounds__(64 * kPrefixLaunchWaves) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
 void attn_prefix_kernel(AttnParams p, InlineMeta im) {
-  static_assert(PrefixShape<D>::W == kPrefixLaunchWaves, "prefix units are the launch's workgroups");
+  static_assert(PrefixShape<D, Q8>::W == kPrefixLaunchWaves, "prefix units are the launch's workgroups");
   const int32_t* meta = p.app.ext ? p.app.ext : im.w;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int n_attn = p.n_units * p.hkv;  // attention waves
@@ -1523,15 +1523,15 @@ void attn_prefix_kernel(AttnParams p, InlineMeta im) {
   const int b = blockIdx.x;
   if (b < n_attn_wg) {
     const int vb = b * kPrefixLaunchWaves + wave;
-    if (vb < n_attn) attn_unit<T, D, NT, false, FUSED, false, true>(p, meta, vb);
+    if (vb < n_attn) attn_unit<T, D, NT, false, FUSED, Q8, true>(p, meta, vb);
     return;
   }
   if (b < n_attn_wg + n_pre) {
-    prefix_unit<T, D, false>(p, b - n_attn_wg);
+    prefix_unit<T, D, Q8>(p, b - n_attn_wg);
     return;
   }
   if constexpr (FUSED)
-    append_work<static_cast<int>(sizeof(T))>(p.app, meta, b - n_attn_wg - n_pre, 64 * kPrefixLaunchWaves);
+    append_work<Q8 ? 1 : static_cast<int>(sizeof(T))>(p.app, meta, b - n_attn_wg - n_pre, 64 * kPrefixLaunchWaves);
 }
 
 // Exact merge of one output row of a split sequence, one 256-thread workgroup
@@ -1614,16 +1614,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
 
 template <typename T, int D, int NT, bool NTL, bool Q8>
 void launch_attn_nt(const AttnParams& p, const InlineMeta& m, hipStream_t stream) {
-  if constexpr (!std::is_same_v<T, float> && !Q8 && !NTL && (D <= 128 ? NT <= 2 : NT == 1)) {
+  if constexpr (!std::is_same_v<T, float> && !NTL && (D <= 128 ? NT <= 2 : NT == 1)) {
     if (p.pre_in_launch) {
       // (app_blocks counts workgroups of the launch's size here)
       const int attn_wg = (p.n_units * p.hkv + kPrefixLaunchWaves - 1) / kPrefixLaunchWaves;
       const dim3 grid(static_cast<unsigned>(attn_wg + p.n_pre_units * p.hkv + (p.t_new > 0 ? p.app_blocks : 0)));
       const dim3 block(64 * kPrefixLaunchWaves);
       if (p.t_new > 0)
-        hipLaunchKernelGGL((attn_prefix_kernel<T, D, NT, true>), grid, block, 0, stream, p, m);
+        hipLaunchKernelGGL((attn_prefix_kernel<T, D, NT, true, Q8>), grid, block, 0, stream, p, m);
       else
-        hipLaunchKernelGGL((attn_prefix_kernel<T, D, NT, false>), grid, block, 0, stream, p, m);
+        hipLaunchKernelGGL((attn_prefix_kernel<T, D, NT, false, Q8>), grid, block, 0, stream, p, m);
       return;
     }
   }
@@ -1712,7 +1712,7 @@ int prefix_units_t(int head_dim) {
 
 // (wider row tiles would not fit the two waves per SIMD the pass needs)
 bool prefix_in_attention_launch(int dtype, int head_dim, int rows) {
-  return (dtype == kBF16 || dtype == kF16) && rows <= (head_dim <= 128 ? 32 : 16);
+  return (dtype == kBF16 || dtype == kF16 || dtype == kFP8) && rows <= (head_dim <= 128 ? 32 : 16);
 }
 
 int prefix_rows_per_unit(int dtype, int head_dim) {

@@ -166,8 +166,9 @@ hipError_t launch_prefix(DType dt, const AttnParams& p, hipStream_t stream);
 // Query rows one workgroup of the shared-prefix pass takes, for a head dim.
 int prefix_rows_per_unit(int dtype, int head_dim);
 // Whether the shared-prefix pass can run inside the attention launch of a
-// call with `rows` query rows per kv head (its workgroups are single waves,
-// as the attention's are, and both fit the same registers).
+// call with `rows` query rows per kv head (four-wave workgroups: the pass's
+// units, and attention workgroups of four single-wave units, all fitting two
+// waves per SIMD).
 bool prefix_in_attention_launch(int dtype, int head_dim, int rows);
 // workgroups of the shared-prefix pass one compute unit holds at once
 int prefix_units_per_cu(int dtype, int head_dim);
