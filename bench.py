@@ -607,7 +607,8 @@ def main():
         # the shared-prefix units ran inside the attention launch: it moves
         # the whole step's bytes (the prefix once, q once)
         attn_name, attn_b = "attn_prefix_kernel", dec_b + (app_b if fused else 0)
-    own = {3: ("prefix_kernel", prefix_b), 0: (attn_name, attn_b), 2: ("append_kernel", app_b), 1: ("merge_kernel", 0)}
+    merge_name = "merge_rows_kernel" if attn_name == "attn_prefix_kernel" else "merge_kernel"
+    own = {3: ("prefix_kernel", prefix_b), 0: (attn_name, attn_b), 2: ("append_kernel", app_b), 1: (merge_name, 0)}
     kernels, kernel_us_step, traffic = [], 0.0, 0
     for k in (3, 2, 0, 1):
         ms, n = kern[k]

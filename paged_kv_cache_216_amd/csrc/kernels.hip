@@ -377,7 +377,10 @@ __device__ inline f32x4 load_device4(__amdgpu_buffer_rsrc_t r, int byte_off) {
 // all RG groups' partitions issued together; partitions C at a time,
 // combined with a running maximum (one chunk: M = max m_q, the weights
 // 2^(m_q - M)).  Chunks past the sequence's partitions weigh 0.
-template <typename T, int D, int C, int RG>
+// (DEV: the partials were written by other waves of this launch and are read
+// at device scope; else a launch boundary lies between, and plain loads see
+// them)
+template <typename T, int D, int C, int RG, bool DEV>
 __device__ inline void merge_rows(const AttnParams& p, const MergeUnit& mu, int kvh, int lane, int r_begin,
                                   int r_end) {
   constexpr int V = D / 64;  // 16-byte column chunks per lane
@@ -408,10 +411,18 @@ __device__ inline void merge_rows(const AttnParams& p, const MergeUnit& mu, int 
         for (int q = 0; q < C; ++q) {
           const int qq = min(q0 + q, P - 1);
           const size_t sl = static_cast<size_t>(base + qq) * p.rows + rr[g];
-          m[g][q] = load_device(p.ws_ml + 2 * sl);
-          l[g][q] = load_device(p.ws_ml + 2 * sl + 1);
+          if constexpr (DEV) {
+            m[g][q] = load_device(p.ws_ml + 2 * sl);
+            l[g][q] = load_device(p.ws_ml + 2 * sl + 1);
+          } else {
+            m[g][q] = p.ws_ml[2 * sl];
+            l[g][q] = p.ws_ml[2 * sl + 1];
+          }
 #pragma unroll
-          for (int v = 0; v < V; ++v) a[g][q][v] = load_device4(racc, static_cast<int>((sl * D + c0 + 4 * v) * 4));
+          for (int v = 0; v < V; ++v)
+            a[g][q][v] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(racc, static_cast<int>((sl * D + c0 + 4 * v) * 4), 0,
+                                                             DEV ? kCacheDeviceScope : 0));
         }
 #pragma unroll
       for (int g = 0; g < RG; ++g) {
@@ -458,20 +469,20 @@ __device__ inline void merge_rows(const AttnParams& p, const MergeUnit& mu, int 
 // fits them.  (The same arithmetic in every shape: chunks of C = 8
 // partitions, or one chunk of 4 when there are at most 4, where the chunk of
 // 8 would add zero weights only.)
-template <typename T, int D>
+template <typename T, int D, bool DEV = true>
 __device__ inline void merge_rows_of(const AttnParams& p, const MergeUnit& mu, int kvh, int lane, int r_begin,
                                      int r_end) {
   if (r_end - r_begin <= 4) {
     if (mu.nparts <= 4)
-      merge_rows<T, D, 4, 1>(p, mu, kvh, lane, r_begin, r_end);
+      merge_rows<T, D, 4, 1, DEV>(p, mu, kvh, lane, r_begin, r_end);
     else
-      merge_rows<T, D, 8, 1>(p, mu, kvh, lane, r_begin, r_end);
+      merge_rows<T, D, 8, 1, DEV>(p, mu, kvh, lane, r_begin, r_end);
   } else if (mu.nparts <= 4) {
-    merge_rows<T, D, 4, 4>(p, mu, kvh, lane, r_begin, r_end);
+    merge_rows<T, D, 4, 4, DEV>(p, mu, kvh, lane, r_begin, r_end);
   } else if (mu.nparts <= 8) {
-    merge_rows<T, D, 8, 2>(p, mu, kvh, lane, r_begin, r_end);
+    merge_rows<T, D, 8, 2, DEV>(p, mu, kvh, lane, r_begin, r_end);
   } else {
-    merge_rows<T, D, 8, 1>(p, mu, kvh, lane, r_begin, r_end);
+    merge_rows<T, D, 8, 1, DEV>(p, mu, kvh, lane, r_begin, r_end);
   }
 }
 
@@ -1068,7 +1079,7 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
   if constexpr (PREFIX) {
     // each row's partial goes to partition u.part of its own sequence (at
     // device scope when the members' merge runs in this launch)
-    const bool dev = p.pre_in_launch != 0;
+    const bool dev = p.pre_in_launch != 0 && p.inline_merge != 0;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const float l = wave_sum_groups(l_run[nt]);
@@ -1799,6 +1810,55 @@ hipError_t launch_merge_t(const AttnParams& p, hipStream_t stream) {
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// Merge of split sequences with at most kInlineMergeParts partitions, as a
+// launch of its own after an attention launch that does not merge (the one
+// that also runs the shared-prefix units): one wave per (split sequence, kv
+// head, 4 query rows), four waves per workgroup, with the in-launch merge's
+// arithmetic.  Every wave's loads leave at once, instead of the merges of a
+// launch's last waves running one after the other in its tail.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_rows_kernel(AttnParams p) {
+  const int lane = threadIdx.x & 63;
+  const int task = static_cast<int>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int groups = (p.rows + 3) / 4;
+  const int per_merge = p.hkv * groups;
+  const int m = task / per_merge;
+  if (m >= p.n_merges) return;
+  const int rem = task - m * per_merge;
+  const int kvh = rem / groups;
+  const int r0 = (rem - kvh * groups) * 4;
+  merge_rows_of<T, D, false>(p, p.merges[m], kvh, lane, r0, min(r0 + 4, p.rows));
+}
+
+template <typename T>
+hipError_t launch_merge_rows_t(const AttnParams& p, hipStream_t stream) {
+  const long long tasks = static_cast<long long>(p.n_merges) * p.hkv * ((p.rows + 3) / 4);
+  const dim3 grid(static_cast<unsigned>((tasks + 3) / 4));
+  switch (p.head_dim) {
+    case 64: hipLaunchKernelGGL((merge_rows_kernel<T, 64>), grid, dim3(256), 0, stream, p); break;
+    case 128: hipLaunchKernelGGL((merge_rows_kernel<T, 128>), grid, dim3(256), 0, stream, p); break;
+    case 256: hipLaunchKernelGGL((merge_rows_kernel<T, 256>), grid, dim3(256), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+int merge_rows_workgroups(const AttnParams& p) {
+  const long long tasks = static_cast<long long>(p.n_merges) * p.hkv * ((p.rows + 3) / 4);
+  return static_cast<int>((tasks + 3) / 4);
+}
+
+hipError_t launch_merge_rows(DType dt, const AttnParams& p, hipStream_t stream) {
+  if (p.n_merges == 0) return hipSuccess;
+  switch (dt) {
+    case kBF16:
+    case kFP8: return launch_merge_rows_t<__bf16>(p, stream);
+    case kF16: return launch_merge_rows_t<_Float16>(p, stream);
+    case kF32: return launch_merge_rows_t<float>(p, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_merge(DType dt, const AttnParams& p, hipStream_t stream) {

@@ -139,7 +139,7 @@ struct AttnParams {
   const PrefixMember* pre_members;
   int n_pre_units;
   // 1: the shared-prefix units run in the attention launch itself, after the
-  // attention units (16-bit pools, in-launch merge)
+  // attention units; the splits are then merged by launch_merge_rows
   int pre_in_launch;
   // Graph steps (graph_units > 0, fused append + attention): the grid is
   // padded to graph_units units and the launch's append workgroups, and the
@@ -160,6 +160,11 @@ constexpr int kInlineMergeParts = 16;
 hipError_t launch_append(const AppendParams& p, const InlineMeta* meta, hipStream_t stream);
 hipError_t launch_attention(DType dt, const AttnParams& p, const InlineMeta* meta, hipStream_t stream);
 hipError_t launch_merge(DType dt, const AttnParams& p, hipStream_t stream);
+// The merge of splits with at most kInlineMergeParts partitions, one wave per
+// (split, kv head, 4 query rows), after an attention launch that runs the
+// shared-prefix units and does not merge; and its workgroup count.
+hipError_t launch_merge_rows(DType dt, const AttnParams& p, hipStream_t stream);
+int merge_rows_workgroups(const AttnParams& p);
 // The shared-prefix pass as a launch of its own, run before launch_attention
 // (when pre_in_launch is 0).
 hipError_t launch_prefix(DType dt, const AttnParams& p, hipStream_t stream);

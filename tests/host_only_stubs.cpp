@@ -28,6 +28,8 @@ int prefix_units_per_cu(int, int) { unreachable("prefix_units_per_cu"); }
 bool prefix_in_attention_launch(int, int, int) { unreachable("prefix_in_attention_launch"); }
 int append_blocks64(const AppendParams&) { unreachable("append_blocks64"); }
 int append_blocks_prefix_launch(const AppendParams&) { unreachable("append_blocks_prefix_launch"); }
+hipError_t launch_merge_rows(DType, const AttnParams&, hipStream_t) { unreachable("launch_merge_rows"); }
+int merge_rows_workgroups(const AttnParams&) { unreachable("merge_rows_workgroups"); }
 int prefix_launch_waves() { unreachable("prefix_launch_waves"); }
 int prefix_rows_per_wave(int) { unreachable("prefix_rows_per_wave"); }
 int max_rows_for_head_dim(int) { unreachable("max_rows_for_head_dim"); }
