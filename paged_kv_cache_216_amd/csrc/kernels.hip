@@ -659,7 +659,11 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
     Op pa[NT];
     float a4[NT][4];
     bool rescale[NT];
-    // scores and online-softmax update for every row tile (needs K only)
+    // Scores of every row tile, then each softmax step for all tiles at once:
+    // the tiles' chains are independent instructions of one block, which the
+    // scheduler interleaves.  Raw scores: the scale (> 0) goes into the
+    // maximum once per row and into each exponent's fused multiply-add.
+    float x[NT][8];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -668,52 +672,63 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
         s0 = MfmaOp<T>::mma(f.k0[s], qop[nt][s], s0);
         s1 = MfmaOp<T>::mma(f.k1[s], qop[nt][s], s1);
       }
-      // raw scores: the scale (> 0) goes into the maximum once per row and into
-      // each exponent's fused multiply-add
-      float x[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[e] = s0[e];
-        x[4 + e] = s1[e];
+        x[nt][e] = s0[e];
+        x[nt][4 + e] = s1[e];
       }
-      if (need_mask) {
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int pos = pos0 + (e >> 2) * kBlk + 4 * grp + (e & 3);
           const bool ok = pos < end && pos <= lim[nt];
-          x[e] = ok ? x[e] : kNegInf;
+          x[nt][e] = ok ? x[nt][e] : kNegInf;
         }
-      }
-      float mt = x[0];
+    }
+    float mt[NT];
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mt = fmax_prop(mt, x[e]);
-      // (scaling by sl2 > 0 commutes with the maximum, rounding included)
-      mt = wave_max_groups(mt) * sl2;
+    for (int nt = 0; nt < NT; ++nt) {
+      mt[nt] = x[nt][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mt[nt] = fmax_prop(mt[nt], x[nt][e]);
+    }
+    // (scaling by sl2 > 0 commutes with the maximum, rounding included)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) mt[nt] = wave_max_groups(mt[nt]) * sl2;
+    float alpha[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
       // The reference maximum of a row moves only when a score exceeds it by
       // more than kMaxSlack (log2 units), so probabilities stay <= 2^kMaxSlack:
       // exact in real arithmetic (acc, l and m stay consistent), no precision
       // lost (bf16 and fp32 keep their relative precision at that size), and
       // the accumulator rescale becomes rare.  A first finite score always
       // sets it (-inf + slack is -inf).
-      const float m_new = (mt > m_run[nt] + kMaxSlack) ? mt : m_run[nt];
+      const float m_new = (mt[nt] > m_run[nt] + kMaxSlack) ? mt[nt] : m_run[nt];
       const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
+      alpha[nt] = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
       float ps = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], sl2, -m_use));
+        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(x[nt][e], sl2, -m_use));
         ps += pe;
         pa[nt][e] = static_cast<T>(pe);
       }
-      l_run[nt] = l_run[nt] * alpha + ps;
+      l_run[nt] = l_run[nt] * alpha[nt] + ps;
       m_run[nt] = m_new;
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
       // While no reference maximum moves, alpha is exactly 1 on every row and
       // the accumulator rescale (a multiply by 1) is skipped for the whole wave.
-      rescale[nt] = __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0;
+      rescale[nt] = __builtin_amdgcn_ballot_w64(alpha[nt] != 1.f) != 0;
       // rescale factors move to the accumulator layout: lane holds rows 4*grp + jj
       if (rescale[nt]) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) a4[nt][jj] = shfl_f(alpha, 4 * grp + jj);
+        for (int jj = 0; jj < 4; ++jj) a4[nt][jj] = shfl_f(alpha[nt], 4 * grp + jj);
       }
     }
     if (pos0 + 2 * kBlk > end) {
