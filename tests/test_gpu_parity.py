@@ -378,7 +378,11 @@ def _check_verify_partition(pair):
     assert prefix_wgs == -(-4096 // pt) * 10 * 8, (pt, prefix_wgs)
     if 8 * 10 * 8 + 128 > resident:
         assert prefix_wgs + 128 <= resident, (pt, prefix_wgs, resident)
-    assert pair.gpu.last_call_stats()["prefix_kv_tokens"] == 4096
+    st = pair.gpu.last_call_stats()
+    assert st["prefix_kv_tokens"] == 4096
+    # the splits (64 members x 8 kv heads x 5 groups of 4 rows) are merged by
+    # a launch of their own, four waves per workgroup
+    assert st["merge_workgroups"] == 64 * 8 * 5 // 4, st
 
 
 def test_full_verify():
