@@ -236,10 +236,13 @@ int pa_append_kv(pa_pool* pool, const int32_t* seq_ids, int n_seq, const int32_t
  *                With partition_tokens = 0 the library only splits when the
  *                workspace is large enough.
  * Shared prefixes: when at least 4 sequences of the call are copy-on-write
- * forks whose first partitions (whole partitions that every query row sees)
- * sit in the same physical blocks, those partitions are computed once for the
- * query rows of all of them, in a launch before the attention launch, so the
- * shared blocks are read once per call instead of once per sequence (blocks
+ * forks that hold at least one whole partition in the same physical blocks
+ * (positions every query row sees), the whole shared prefix is computed once
+ * for the query rows of all of them -- inside the attention launch, followed
+ * by a launch that merges the splits, when one unit takes all query rows of a
+ * (sequence, kv head) and no sequence has more than 16 partitions; else in a
+ * launch before the attention launch -- so the shared blocks are read once
+ * per call instead of once per sequence (blocks
  * shared by sequences of one prompt: "PagedAttention, décodage spéculatif,
  * MoE et Blackwell", section 1; kenji.blog page, section 4.2; reusing the KV
  * cache of a common prefix: ranksignal.fr post 218, "Mettre en cache").
@@ -430,8 +433,8 @@ int pa_last_partition(const pa_pool* pool, int* partition_tokens, int* prefix_un
  * first call. */
 typedef struct pa_call_stats {
   int32_t partition_tokens;
-  int32_t prefix_workgroups;     /* shared-prefix launch (0: none) */
-  int32_t attention_workgroups;  /* attention workgroups of the attention launch */
+  int32_t prefix_workgroups;     /* shared-prefix units, in their own launch or the attention launch (0: none) */
+  int32_t attention_workgroups;  /* attention units of the attention launch (units x kv heads) */
   int32_t append_workgroups;     /* append workgroups inside that launch (fused append) */
   int32_t merge_workgroups;      /* separate merge launch (0: none, or merged inside) */
   int32_t reserved;
