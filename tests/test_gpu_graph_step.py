@@ -36,12 +36,13 @@ def _buffers(n, n_new, w, dtype):
     }
 
 
-@pytest.mark.parametrize("dtype,g,n_new", [("bf16", 4, 1), ("f16", 8, 1), ("bf16", 4, 5), ("fp8", 4, 1)])
-def test_graph_steps_replay_like_eager_calls(dtype, g, n_new):
-    print(f"graph steps {dtype} G={g} n_new={n_new}", flush=True)
+@pytest.mark.parametrize("dtype,g,n_new,d", [("bf16", 4, 1, 128), ("f16", 8, 1, 128), ("bf16", 4, 5, 128),
+                                             ("fp8", 4, 1, 128), ("bf16", 4, 1, 64), ("f16", 2, 3, 256)])
+def test_graph_steps_replay_like_eager_calls(dtype, g, n_new, d):
+    print(f"graph steps {dtype} G={g} n_new={n_new} D={d}", flush=True)
     wd = "bf16" if dtype == "fp8" else dtype
     lens = [int(x) for x in np.clip(np.rint(np.random.default_rng(90).lognormal(np.log(200), 1.0, 20)), 16, 1500)]
-    w = make_custom(lengths=lens, num_q_heads=4 * g, num_kv_heads=4, head_dim=128, dtype=wd, seed=91)
+    w = make_custom(lengths=lens, num_q_heads=4 * g, num_kv_heads=4, head_dim=d, dtype=wd, seed=91)
     w.max_blocks_per_seq = 160
     nb = 2000
     order = np.random.default_rng(92).permutation(nb)
