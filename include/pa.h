@@ -341,9 +341,11 @@ int pa_append_attend(pa_pool* pool, const int32_t* seq_ids, int n_seq, int n_new
  *
  * pa_graph_prepare: the step's host bookkeeping and everything that cannot be
  *   replayed, eagerly on `stream` -- pending table changes, and the whole
- *   append when it needs copy-on-write copies -- then one copy, on `stream`,
- *   of the step's metadata (lengths, slots of the new rows, table updates) and
- *   work plan into a buffer that the library keeps for the step's class.  The
+ *   append when it needs copy-on-write copies -- then small kernels on
+ *   `stream` write the step's metadata (lengths, slots of the new rows, table
+ *   and length updates) and, when it changed, its work plan into a buffer that
+ *   the library keeps for the step's class (allocated on the class's first
+ *   prepare).  The
  *   class is the number of work units rounded up to a power of two (at least
  *   16), with n_new: *class_units (may be NULL) returns it.  Arguments as
  *   pa_append_attend, with these limits: 16-bit or E4M3 pools; (num_q_heads /
@@ -361,7 +363,11 @@ int pa_append_attend(pa_pool* pool, const int32_t* seq_ids, int n_seq, int n_new
  *   pa_graph_prepare of the same class runs that step.  Replays use the
  *   buffers (q, out, lse, k_new, v_new, workspace) and the scale given to the
  *   prepare before the capture: pass the same ones to every prepare of a
- *   class.  PA_ERR_STATE before any prepare. */
+ *   class.  PA_ERR_STATE before any prepare.
+ * Ordering: the device's table and length mirrors receive the step's updates
+ * only when its launch (or replay) runs, so run it on `stream` after each
+ * prepare, before any other call on the pool; replaying an older step after a
+ * newer prepare of the same class runs the newer one. */
 int pa_graph_prepare(pa_pool* pool, const int32_t* seq_ids, int n_seq, int n_new, const void* k_new,
                      const void* v_new, int num_q_heads, float scale, const void* q, void* out, float* lse,
                      int partition_tokens, void* workspace, size_t ws_bytes, void* stream, int* class_units);
