@@ -62,3 +62,59 @@ def test_random_configuration(c):
     torch.cuda.synchronize()
     ro, rl = oracle_decode(pair, seqs, w.q, w.scale, k_draft=c["kd"])
     assert_close(out, lse, ro, rl, c["dtype"], "random configuration")
+
+
+def _fused_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for case in range(n):
+        d = int(rng.choice([64, 128, 256]))
+        g = int(rng.choice([1, 2, 4, 8]))
+        kd = int(rng.choice([1, 1, 2, 3, 5]))
+        if g * kd > (64 if d <= 128 else 32):
+            kd = 1
+        prefix = int(rng.choice([0, 0, 300, 530, 1100, 2100]))
+        b = int(rng.integers(4, 10)) if prefix else int(rng.integers(1, 10))
+        out.append(dict(
+            D=d, hkv=int(rng.choice([1, 2, 4, 8])), G=g, kd=kd, dtype=str(rng.choice(["bf16", "f16", "fp8"])),
+            prefix=prefix, lengths=[int(x) for x in rng.integers(0 if prefix else 1, 1400, size=b)],
+            pt=int(rng.choice([0, 0, 32, 64, 256, 512, 608])), rising=bool(rng.random() < 0.3),
+            scales=(rng.uniform(0.01, 3.0, size=8).astype(np.float32), rng.uniform(0.01, 3.0, size=8).astype(np.float32)),
+            seed=6000 + case))
+    return out
+
+
+@pytest.mark.parametrize("c", _fused_cases(16, 20261204), ids=lambda c: f"D{c['D']}-h{c['hkv']}-g{c['G']}-k{c['kd']}-"
+                         f"{c['dtype']}-p{c['prefix']}-pt{c['pt']}{'-rising' if c['rising'] else ''}")
+def test_random_fused_step(c):
+    """The same kind of draws through pa_append_attend (append and attention in
+    one call: fused when one unit takes all query rows, the shared-prefix units
+    inside the attention launch and the merge launch after it), with kv heads up
+    to 8 and, in some cases, scores that rise after the first pair."""
+    from workloads.synth import with_rising_scores
+
+    print(f"random fused {c}", flush=True)
+    wd = "bf16" if c["dtype"] == "fp8" else c["dtype"]
+    w = make_custom(lengths=c["lengths"], mode="verify" if c["kd"] > 1 else "append_decode",
+                    num_q_heads=c["G"] * c["hkv"], num_kv_heads=c["hkv"], head_dim=c["D"], dtype=wd, seed=c["seed"],
+                    k_draft=c["kd"], prefix_len=c["prefix"])
+    if c["rising"]:
+        w = with_rising_scores(w, every=2)
+    if c["dtype"] == "fp8":
+        pair = Pair(w, cache_dtype="fp8", kv_scales=(c["scales"][0][:c["hkv"]], c["scales"][1][:c["hkv"]]))
+    else:
+        pair = Pair(w)
+    pair.fill()
+    seqs = list(range(w.batch))
+    n, t, hkv, d = len(seqs), w.new_k.shape[1], c["hkv"], c["D"]
+    kn, vn = w.new_k.reshape(-1, hkv, d), w.new_v.reshape(-1, hkv, d)
+    ws = pair.gpu.make_workspace(n, w.num_q_heads, int(max(pair.model.length(s) for s in seqs)) + t,
+                                 k_draft=c["kd"], partition_tokens=c["pt"])
+    if ws is not None:
+        ws.fill_(float("nan"))
+    out, lse = pair.gpu.append_attend(seqs, to_torch(kn, wd), to_torch(vn, wd), to_torch(w.q, wd).contiguous(),
+                                      w.scale, partition_tokens=c["pt"], workspace=ws)
+    pair.model.append(seqs, [t] * n, kn, vn)
+    pair.check_pools_and_tables()
+    ro, rl = oracle_decode(pair, seqs, w.q, w.scale, k_draft=c["kd"])
+    assert_close(out, lse, ro, rl, c["dtype"], "random fused step")
