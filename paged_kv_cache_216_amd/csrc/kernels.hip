@@ -16,11 +16,18 @@
 //                    long verifies: four waves share each pair of blocks through
 //                    an LDS ring filled by buffer loads with an LDS destination.
 //  prefix_kernel     the partitions of a prefix shared by copy-on-write forks,
-//                    once for the query rows of all of them.
+//                    once for the query rows of all of them (four waves per
+//                    workgroup, sharing each pair through the same LDS ring).
+//  attn_prefix_kernel  attention units and shared-prefix units (and a fused
+//                    append) in one launch of four-wave workgroups.
+//  merge_rows_kernel the merge of short splits as a launch of its own, after
+//                    attn_prefix_kernel: one wave per (split, kv head, 4 rows).
 //  merge_kernel      exact log-sum-exp merge of the partitions of split
 //                    contexts, as a separate launch for long splits (each XCD
 //                    has its own L2, so merging many partitions inside the
 //                    attention launch would keep one wave busy after the rest).
+//  (graph steps run attn_append_kernel with its grid padded to a batch class,
+//  its counts read from the step's metadata in device memory.)
 //
 // The pages describe the method (16-token blocks reached through a table inside
 // the attention kernel: "PagedAttention, décodage spéculatif, MoE et Blackwell",
