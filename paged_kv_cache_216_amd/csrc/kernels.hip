@@ -661,16 +661,20 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
   using LFrag = std::conditional_t<Q8, Frag8, Frag>;
   // Scores, online softmax and PV for the 32 tokens starting at pos0; tokens at
   // or beyond `end` are masked (and their V zeroed: such slots may hold anything).
-  auto process = [&](Frag& f, int pos0, int end) {
-    const bool need_mask = (pos0 + 2 * kBlk - 1 > mask_from) || (pos0 + 2 * kBlk > end);
+  // Three stages, so that a pipelined loop can issue the score MFMAs of one
+  // pair under the softmax of the previous one:
+  //   qk:   raw scores S^T = K Q^T of every row tile (the scale (> 0) goes into
+  //         the maximum once per row and into each exponent's fused multiply-add)
+  //   soft: masks, the online-softmax update of m and l, and P in the operand type
+  //   pv:   O = diag(alpha) O + P V
+  // Within a stage each step runs for all tiles at once: the tiles' chains are
+  // independent instructions of one block, which the scheduler interleaves.
+  struct Soft {
     Op pa[NT];
     float a4[NT][4];
     bool rescale[NT];
-    // Scores of every row tile, then each softmax step for all tiles at once:
-    // the tiles' chains are independent instructions of one block, which the
-    // scheduler interleaves.  Raw scores: the scale (> 0) goes into the
-    // maximum once per row and into each exponent's fused multiply-add.
-    float x[NT][8];
+  };
+  auto qk = [&](const Frag& f, float (&x)[NT][8]) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -685,6 +689,11 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
         x[nt][4 + e] = s1[e];
       }
     }
+  };
+  auto needs_mask = [&](int pos0, int end) { return (pos0 + 2 * kBlk - 1 > mask_from) || (pos0 + 2 * kBlk > end); };
+  // masks, the update of m and l, and P; alpha = 2^(m_old - m_new) per row
+  // tile (lane col holds row col)
+  auto soft_core = [&](float (&x)[NT][8], int pos0, int end, bool need_mask, Op (&pa)[NT], float (&alpha)[NT]) {
     if (need_mask) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -705,7 +714,6 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
     // (scaling by sl2 > 0 commutes with the maximum, rounding included)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) mt[nt] = wave_max_groups(mt[nt]) * sl2;
-    float alpha[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       // The reference maximum of a row moves only when a score exceeds it by
@@ -727,17 +735,26 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       l_run[nt] = l_run[nt] * alpha[nt] + ps;
       m_run[nt] = m_new;
     }
+  };
+  auto rescale_of = [&](const float (&alpha)[NT], Soft& sm) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       // While no reference maximum moves, alpha is exactly 1 on every row and
       // the accumulator rescale (a multiply by 1) is skipped for the whole wave.
-      rescale[nt] = __builtin_amdgcn_ballot_w64(alpha[nt] != 1.f) != 0;
+      sm.rescale[nt] = __builtin_amdgcn_ballot_w64(alpha[nt] != 1.f) != 0;
       // rescale factors move to the accumulator layout: lane holds rows 4*grp + jj
-      if (rescale[nt]) {
+      if (sm.rescale[nt]) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) a4[nt][jj] = shfl_f(alpha[nt], 4 * grp + jj);
+        for (int jj = 0; jj < 4; ++jj) sm.a4[nt][jj] = shfl_f(alpha[nt], 4 * grp + jj);
       }
     }
+  };
+  auto soft = [&](float (&x)[NT][8], int pos0, int end, bool need_mask, Soft& sm) {
+    float alpha[NT];
+    soft_core(x, pos0, end, need_mask, sm.pa, alpha);
+    rescale_of(alpha, sm);
+  };
+  auto pv = [&](Frag& f, int pos0, int end, const Soft& sm) {
     if (pos0 + 2 * kBlk > end) {
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
@@ -748,18 +765,46 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
     // O = diag(alpha) O + P V
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      if (rescale[nt]) {
+      if (sm.rescale[nt]) {
 #pragma unroll
         for (int c = 0; c < DC; ++c)
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) acc[nt][c][jj] *= a4[nt][jj];
+          for (int jj = 0; jj < 4; ++jj) acc[nt][c][jj] *= sm.a4[nt][jj];
       }
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        const Op vb = __builtin_bit_cast(Op, u32x4{f.v0[c][0], f.v0[c][1], f.v1[c][0], f.v1[c][1]});
+        acc[nt][c] = MfmaOp<T>::mma(sm.pa[nt], vb, acc[nt][c]);
+      }
+    }
+  };
+  // pieces of the PV step for the pipelined loop: V masked past the end, the
+  // MFMAs
+  auto mask_v = [&](Frag& f, int pos0, int end) {
+    if (pos0 + 2 * kBlk > end) {
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        f.v0[c] = mask_v16(f.v0[c], pos0 + 4 * grp, end);
+        f.v1[c] = mask_v16(f.v1[c], pos0 + kBlk + 4 * grp, end);
+      }
+    }
+  };
+  auto pv_mma = [&](const Frag& f, const Op (&pa)[NT]) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
         const Op vb = __builtin_bit_cast(Op, u32x4{f.v0[c][0], f.v0[c][1], f.v1[c][0], f.v1[c][1]});
         acc[nt][c] = MfmaOp<T>::mma(pa[nt], vb, acc[nt][c]);
       }
-    }
+  };
+  auto process = [&](Frag& f, int pos0, int end) {
+    const bool need_mask = needs_mask(pos0, end);
+    float x[NT][8];
+    qk(f, x);
+    Soft sm;
+    soft(x, pos0, end, need_mask, sm);
+    pv(f, pos0, end, sm);
   };
 
   // The table row, 64 entries per chunk, one per lane; each chunk's successor
@@ -839,10 +884,10 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       constexpr int kPair = 4 * kPageBytes;
       constexpr int kPer = kPair / (16 * 64 * W);  // 16-byte chunks per thread
       constexpr int kChunksPerPage = kPageBytes / 16;
-      constexpr int kRing = 4;
+      constexpr int kRing = kPair <= 16384 ? 5 : 4;
       static_assert(kPer * 16 * 64 * W == kPair, "pair image must split evenly");
       static_assert(kChunksPerPage == 64 * kPer, "a wave's loads cover one page");
-      static_assert(kRing >= 2 && kRing <= 4 && (kRing - 2) * kPer <= 63, "the waits below cover up to two later pairs");
+      static_assert(kRing >= 3 && kRing <= 5 && (kRing - 2) * kPer <= 63, "the waits below cover up to three later pairs");
       __shared__ __attribute__((aligned(16))) char lds[kRing][kPair];
       static_assert(W == 4, "one wave per page of the pair image");
       const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
@@ -870,9 +915,9 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
               gc * 16, 0, 0, NTL ? 2 : 0);
         }
       };
-      auto lfrag = [&](Frag& f, int b) {
+      // fragments of a pair image: K (the score operands), then V (the PV operands)
+      auto lfrag_k = [&](Frag& f, int b) {
         const char* kb = lds[b];
-        const char* vb = lds[b] + 2 * kPageBytes;
         if constexpr (Q8) {
           // the 8-bit operands at the offsets of the pool loads, turned into bf16
 #pragma unroll
@@ -881,12 +926,6 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
             f.k0[s] = __builtin_bit_cast(Op, fp8x8_to_bf16(*reinterpret_cast<const u32x2*>(kb + o)));
             f.k1[s] = __builtin_bit_cast(Op, fp8x8_to_bf16(*reinterpret_cast<const u32x2*>(kb + kPageBytes + o)));
           }
-#pragma unroll
-          for (int c = 0; c < DC; ++c) {
-            const int o = (16 * c + col) * kBlk + 4 * grp;
-            f.v0[c] = fp8x4_to_bf16(*reinterpret_cast<const uint32_t*>(vb + o));
-            f.v1[c] = fp8x4_to_bf16(*reinterpret_cast<const uint32_t*>(vb + kPageBytes + o));
-          }
         } else {
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
@@ -894,6 +933,18 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
             f.k0[s] = __builtin_bit_cast(Op, *reinterpret_cast<const u32x4*>(kb + o));
             f.k1[s] = __builtin_bit_cast(Op, *reinterpret_cast<const u32x4*>(kb + kPageBytes + o));
           }
+        }
+      };
+      auto lfrag_v = [&](Frag& f, int b) {
+        const char* vb = lds[b] + 2 * kPageBytes;
+        if constexpr (Q8) {
+#pragma unroll
+          for (int c = 0; c < DC; ++c) {
+            const int o = (16 * c + col) * kBlk + 4 * grp;
+            f.v0[c] = fp8x4_to_bf16(*reinterpret_cast<const uint32_t*>(vb + o));
+            f.v1[c] = fp8x4_to_bf16(*reinterpret_cast<const uint32_t*>(vb + kPageBytes + o));
+          }
+        } else {
 #pragma unroll
           for (int c = 0; c < DC; ++c) {
             const int o = ((grp >> 1) * D + 16 * c + col) * 16 + 8 * (grp & 1);
@@ -907,6 +958,18 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       constexpr int kNoOther = (7 << 4) | (15 << 8);
       constexpr int kWait1 = kNoOther | (kPer & 15) | ((kPer >> 4) << 14);
       constexpr int kWait2 = kNoOther | ((2 * kPer) & 15) | ((2 * kPer) >> 4 << 14);
+      constexpr int kWait3 = kNoOther | ((3 * kPer) & 15) | ((3 * kPer) >> 4 << 14);
+      // this wave's loads have landed but for those of the last `later` pairs issued
+      auto wait_later = [&](int later) {
+        if (later >= 3)
+          __builtin_amdgcn_s_waitcnt(kWait3);
+        else if (later == 2)
+          __builtin_amdgcn_s_waitcnt(kWait2);
+        else if (later == 1)
+          __builtin_amdgcn_s_waitcnt(kWait1);
+        else
+          __builtin_amdgcn_s_waitcnt(kNoOther);
+      };
       // Loads into registers (queries, table entries) complete here, before
       // the ring starts: otherwise the compiler's waits for them sit inside
       // the loop, where their counts would also cover the pairs in flight.
@@ -914,25 +977,81 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
 #pragma unroll
       for (int r = 0; r < kRing - 1; ++r)
         if (r < npairs) dma(r, r);
-      for (int pj = 0; pj < npairs; ++pj) {
-        // This wave's share of pair pj has landed (only the loads of the
-        // pairs after it may still run); after the barrier every wave's share
-        // has, and every wave has read the image of pair pj - 1 (its
-        // fragments fed the MFMAs before the wave got here), which the load
-        // of pair pj + kRing - 1 then overwrites.  A bare s_barrier: a fence
-        // would make the compiler wait for the later pairs' loads as well.
-        const int later = min(npairs - 1 - pj, kRing - 2);  // pairs issued after pj
-        if (later >= 2)
-          __builtin_amdgcn_s_waitcnt(kWait2);
-        else if (later == 1)
-          __builtin_amdgcn_s_waitcnt(kWait1);
-        else
-          __builtin_amdgcn_s_waitcnt(kNoOther);
+      // Software pipeline: the PV MFMAs of pair pj - 1 are interleaved with
+      // the softmax of pair pj, which does not depend on them, so the matrix
+      // core works under the softmax's vector instructions (acc sees the same
+      // updates in the same order: alpha_q, then P_q V_q, for q = 0, 1, ...).
+      // Pair q sits in ring slot q % kRing; its V fragments are read into
+      // registers in iteration q.  At the barrier of iteration pj this wave's
+      // share of pair pj has landed (only the loads of the pairs after it may
+      // still run), so every wave's has, and every wave has read the image of
+      // pair pj - 1, which the load of pair pj + kRing - 1 then overwrites.
+      // A bare s_barrier: a fence would make the compiler wait for the later
+      // pairs' loads as well.  The empty asm statement after it keeps the
+      // compiler from moving the LDS reads above it.
+      // The end of an iteration (softmax, PV MFMAs, the next V reads) is
+      // branch-free, so that the interleaving holds; the rare steps with
+      // branches (masking V past the end, rescaling acc when a reference
+      // maximum moved) run at the start of the next iteration.
+      Frag fv;           // V of the previous pair
+      Op pp[NT];         // its P
+      float ap[NT];      // its alpha (lane col: row col)
+      bool rp[NT];       // whether any alpha of the tile differs from 1
+      int pos_prev = 0;  // its first position
+      auto finish_prev = [&]() {
+        mask_v(fv, pos_prev, pool_end);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          if (rp[nt]) {
+            float a4[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) a4[jj] = shfl_f(ap[nt], 4 * grp + jj);
+#pragma unroll
+            for (int c = 0; c < DC; ++c)
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) acc[nt][c][jj] *= a4[jj];
+          }
+        }
+      };
+      auto step = [&](int pj, auto has_prev) {
+        constexpr bool kPrev = decltype(has_prev)::value;
+        const int pos0 = base_pos + 2 * pj * kBlk;
+        const bool mask = needs_mask(pos0, pool_end);
+        wait_later(min(npairs - 1 - pj, kRing - 2));
         __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
         if (pj + kRing - 1 < npairs) dma(pj + kRing - 1, (pj + kRing - 1) % kRing);
-        Frag f;
-        lfrag(f, pj % kRing);
-        process(f, base_pos + 2 * pj * kBlk, pool_end);
+        if constexpr (kPrev) finish_prev();
+        Frag fk;
+        lfrag_k(fk, pj % kRing);
+        float x[NT][8];
+        qk(fk, x);
+        Op pa[NT];
+        float alpha[NT];
+        soft_core(x, pos0, pool_end, mask, pa, alpha);
+        if constexpr (kPrev) {
+          pv_mma(fv, pp);
+          // one PV MFMA, then a few softmax instructions, and so on
+#pragma unroll
+          for (int i = 0; i < NT * DC; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+          }
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          rp[nt] = __builtin_amdgcn_ballot_w64(alpha[nt] != 1.f) != 0;
+          ap[nt] = alpha[nt];
+          pp[nt] = pa[nt];
+        }
+        lfrag_v(fv, pj % kRing);
+        pos_prev = pos0;
+      };
+      if (npairs > 0) step(0, std::false_type{});
+      for (int pj = 1; pj < npairs; ++pj) step(pj, std::true_type{});
+      if (npairs > 0) {
+        finish_prev();
+        pv_mma(fv, pp);
       }
       __syncthreads();  // the next table chunk refills the ring
     } else if constexpr (Q8) {
