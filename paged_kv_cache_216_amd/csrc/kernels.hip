@@ -14,7 +14,9 @@
 //                    v_new instead of the pool.
 //  tile_kernel       many query rows per (sequence, kv head) -- chunked prefill,
 //                    long verifies: four waves share each pair of blocks through
-//                    an LDS ring filled by buffer loads with an LDS destination.
+//                    an LDS ring filled by buffer loads with an LDS destination;
+//                    each wave's loop is software-pipelined (the PV MFMAs of one
+//                    pair run under the softmax of the next).
 //  prefix_kernel     the partitions of a prefix shared by copy-on-write forks,
 //                    once for the query rows of all of them (four waves per
 //                    workgroup, sharing each pair through the same LDS ring).
