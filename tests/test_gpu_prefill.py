@@ -85,6 +85,35 @@ def test_prefill_long_context_crosses_table_chunks(dtype, head_dim, g, chunk, ca
     assert_close(out, lse, ro, rl, dtype, f"prefill long C={chunk}")
 
 
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_row_tiles_short_last_table_chunk(cache):
+    """Row tiles whose table row ends just past a 64-entry chunk: the second
+    chunk's ring holds one pair (65 and 66 blocks) or two (67 blocks), and a
+    unit of exactly 64 blocks ends on the boundary.  The pipelined ring loop
+    is then all prologue and epilogue: its first step, the PV of the last
+    pair after the loop, and a V mask on a pair past the end.  160 query rows
+    per kv head (two tiles of 128; the second tile's units see 8 positions
+    more than the first's), unsplit.  Outputs and lse against the oracle for
+    every chunk token and query head."""
+    _say(f"row tiles, short last table chunk, {cache}")
+    chunk = 40
+    w = make_custom(lengths=[985, 1001, 1017, 984], mode="verify", num_q_heads=8, num_kv_heads=2, head_dim=128,
+                    dtype="bf16", seed=97, k_draft=chunk)
+    kw = {}
+    if cache == "fp8":
+        kw = dict(cache_dtype="fp8", kv_scales=(np.array([0.02, 0.5], np.float32), np.array([1.5, 0.03], np.float32)))
+    pair = Pair(w, **kw)
+    pair.fill()
+    pair.append_step_rows()
+    pair.check_pools_and_tables()
+    seqs = list(range(w.batch))
+    assert [int(pair.model.length(s)) for s in seqs] == [1025, 1041, 1057, 1024]
+    out, lse = _prefill(pair, seqs, 4096)
+    torch.cuda.synchronize()
+    ro, rl = oracle_decode(pair, seqs, w.q, w.scale, k_draft=chunk)
+    assert_close(out, lse, ro, rl, cache, f"row tiles, short last chunk, {cache}")
+
+
 def test_prefill_equals_verify_bitwise_and_repeats():
     """pa_prefill is pa_verify with k_draft = chunk: bitwise equal results,
     and a second identical call repeats them."""
