@@ -359,10 +359,6 @@ __device__ inline float load_device(const float* a) {
 
 constexpr int kCacheDeviceScope = 16;  // buffer-instruction cache policy: sc1
 
-__device__ inline f32x4 load_device4(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCacheDeviceScope));
-}
-
 // Merge of a split (sequence, kv head) inside the attention launch, by the
 // wave that arrives last (parts <= kInlineMergeParts; one unit takes all the
 // query rows of a (sequence, kv head)).
