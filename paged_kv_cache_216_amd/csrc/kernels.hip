@@ -1073,7 +1073,7 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
         }
         process(f, pos0, pool_end);
       };
-      if constexpr (D * NT <= 256) {
+      if constexpr (D * NT <= 256 && !ONE_PAIR) {
         Frag8 ra, rb;
         load(ra, 0);
         for (int pj = 0; pj < npairs; pj += 2) {
@@ -1083,7 +1083,7 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
           load(ra, pj + 2);
           run(rb, base_pos + (2 * pj + 2) * kBlk);
         }
-      } else {  // wide tiles: the registers hold one pair in flight
+      } else {  // wide tiles, and the launch beside the shared-prefix pass: one pair in flight
         for (int pj = 0; pj < npairs; ++pj) {
           Frag8 r;
           load(r, pj);
@@ -1768,18 +1768,19 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
   }
 }
 
-// The fused append + single-tile 16-bit decode at D = 128 holds two waves per
-// SIMD by its registers, eight per CU.  Its launches reserve 24 KiB of LDS
-// that the kernel does not use, so that a CU holds six: fewer page requests
-// queue in the memory system, and HBM delivers more of them.  (Measured on
-// MI355X, batch-256 step: 63.9-64.5 us at eight waves per CU, 63.8-64.1 at
-// seven, 63.1-63.5 at six, 64.8-65.1 at five and four.  E4M3 pools, whose
-// units are latency-bound, lose at six (45.9 -> 46.6 us); so does the plain
-// decode launch over 8 x 32,768 tokens (176 -> 180 us), while the 70B-like
-// one is unchanged.)
+// The fused append + single-tile decode at D = 128 holds two waves per SIMD
+// by its registers, eight per CU.  Its launches reserve LDS that the kernel
+// does not use, so that a CU holds six (16-bit pools) or seven (E4M3): fewer
+// page requests queue in the memory system, and HBM delivers more of them.
+// (Measured on MI355X, batch-256 step, 16-bit: 63.9-64.5 us at eight waves
+// per CU, 63.8-64.1 at seven, 63.1-63.5 at six, 64.8-65.1 at five and four;
+// E4M3, whose units are more latency-bound: 46.1-46.3 at eight, 45.4-45.5 at
+// seven, 46.6 at six.  The plain decode launch over 8 x 32,768 tokens loses
+// at six (176 -> 180 us) and the 70B-like one does not move, so they keep
+// eight.)
 template <typename T, int D, int NT, bool Q8>
 constexpr unsigned fused_decode_lds() {
-  return (!std::is_same_v<T, float> && !Q8 && D == 128 && NT == 1) ? 24576u : 0u;
+  return (!std::is_same_v<T, float> && D == 128 && NT == 1) ? (Q8 ? 22528u : 24576u) : 0u;
 }
 
 template <typename T, int D, int NT, bool NTL, bool Q8>
