@@ -1776,8 +1776,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
 // per CU, 63.8-64.1 at seven, 63.1-63.5 at six, 64.8-65.1 at five and four;
 // E4M3, whose units are more latency-bound: 46.1-46.3 at eight, 45.4-45.5 at
 // seven, 46.6 at six.  The plain decode launch over 8 x 32,768 tokens loses
-// at six (176 -> 180 us) and the 70B-like one does not move, so they keep
-// eight.)
+// at six and at seven (176 -> 180-181 us) and the 70B-like one does not
+// move, so they keep eight.)
 template <typename T, int D, int NT, bool Q8>
 constexpr unsigned fused_decode_lds() {
   return (!std::is_same_v<T, float> && D == 128 && NT == 1) ? (Q8 ? 22528u : 24576u) : 0u;
