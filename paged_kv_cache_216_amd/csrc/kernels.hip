@@ -659,8 +659,8 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
   using LFrag = std::conditional_t<Q8, Frag8, Frag>;
   // Scores, online softmax and PV for the 32 tokens starting at pos0; tokens at
   // or beyond `end` are masked (and their V zeroed: such slots may hold anything).
-  // Three stages, so that a pipelined loop can issue the score MFMAs of one
-  // pair under the softmax of the previous one:
+  // Three stages, so that the pipelined ring loop (row tiles, shared-prefix
+  // pass) can run the PV MFMAs of one pair under the softmax of the next:
   //   qk:   raw scores S^T = K Q^T of every row tile (the scale (> 0) goes into
   //         the maximum once per row and into each exponent's fused multiply-add)
   //   soft: masks, the online-softmax update of m and l, and P in the operand type
