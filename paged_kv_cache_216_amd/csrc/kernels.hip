@@ -1029,7 +1029,13 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
         Frag fk;
         lfrag_k(fk, pj % kRing);
         float x[NT][8];
+        // The score MFMAs go at a raised wave priority: while a wave issues
+        // them, the other wave of its SIMD (another workgroup's) fills the
+        // vector unit with its softmax.  (Measured on MI355X: prefill tiles
+        // 315 -> 304 us, the verify launch 52.4 -> 51.3 us.)
+        __builtin_amdgcn_s_setprio(1);
         qk(fk, x);
+        __builtin_amdgcn_s_setprio(0);
         Op pa[NT];
         float alpha[NT];
         soft_core(x, pos0, pool_end, mask, pa, alpha);
