@@ -416,7 +416,7 @@ def measured_traffic(workload: str, kernel: str):
 
 def copy_reference():
     """A plain 1 GiB device-to-device copy on the same GPU, timed with events
-    after the timed region: what a simple streaming kernel reaches on this machine
+    after the timed region: what a simple streaming kernel reaches on this GPU
     (bytes read + written / time), as context for the fraction of the 8 TB/s
     specification the attention reaches."""
     import torch
