@@ -882,13 +882,13 @@ __device__ inline void attn_body16(const AttnParams& p, const Unit& u, int kvh) 
       constexpr int kPair = 4 * kPageBytes;
       constexpr int kPer = kPair / (16 * 64 * W);  // 16-byte chunks per thread
       constexpr int kChunksPerPage = kPageBytes / 16;
-      // Four images; five for the E4M3 shared-prefix pass.  (Measured on
-      // MI355X with the pipelined loop: bf16 prefill tiles 313-314 us with
-      // five, 308 with four, 309 with three; bf16 verify 61.1-61.7 / 60.8-61.1
-      // / 61.0-61.5 us; E4M3 prefill tiles 342-343 / 338-339 / 340 us; E4M3
-      // verify 67.0-67.5 / 68.2-68.3 / 68.0 us.  Pages further ahead queue
-      // in the memory system.)
-      constexpr int kRing = (Q8 && PREFIX) ? 5 : 4;
+      // Four images.  (Measured on MI355X with the pipelined loop: bf16
+      // prefill tiles 313-314 us with five, 308 with four, 309 with three;
+      // bf16 verify 61.1-61.7 / 60.8-61.1 / 61.0-61.5 us; E4M3 prefill tiles
+      // 342-343 / 338-339 / 340 us; E4M3 verify, its attention units holding
+      // one pair: 60.6-61.0 with five or four.  Pages further ahead queue in
+      // the memory system.)
+      constexpr int kRing = 4;
       static_assert(kPer * 16 * 64 * W == kPair, "pair image must split evenly");
       static_assert(kChunksPerPage == 64 * kPer, "a wave's loads cover one page");
       static_assert(kRing >= 3 && kRing <= 5 && (kRing - 2) * kPer <= 63, "the waits below cover up to three later pairs");
